@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one attn_fwd call over the whole workload (every step of the
+method runs inside it): the default workload is causal GQA, B=4, Hq=32,
+Hkv=8, S=4096, d=128, bf16. Inputs are seeded synthetic N(0,1) tensors already
+resident in HBM before timing starts. Prints one JSON line with the
+causal-adjusted TFLOP/s, the roofline of the kernel (achieved / peak dense
+MFMA rate, from HIP events around every launch on the launch stream) and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+
+Timing mirrors the codelab's benchmark helper ("Accelerate attention on GPU
+with cuDNN and TransformerEngine", section 8: warm-up calls first, inputs
+already on the device, warm caches), with device events instead of host time.
+
+Other modes (for profiling runs):
+    --no-cpu-baseline        skip the oracle timing
+    --copy-calibration MIB   run a plain device copy of MIB MiB (to calibrate HBM byte counters)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of MFMA peak, 1 MI355X"
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+KERNEL_SOURCES = ["kernel_common.h", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "scaled_dot_product_18_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_name(w) -> str:
+    if w.dtype == "f32":
+        return "attn_fwd_f32_kernel"
+    return "attn_fwd_mfma_kernel"
+
+
+def traffic_from_profiles(w):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float = 15.0) -> dict:
+    """Time the fp64 oracle on whole (batch, head) pairs of the same inputs until the budget is spent."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import e4m3
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = 1
+    G = w.Hq // w.Hkv
+
+    def as64(t, name):
+        if w.dtype == "fp8":
+            return e4m3.decode(t.numpy()) * inp["descale_" + name]
+        return t.to(torch.float64).numpy()
+
+    heads = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            q = as64(inp["q"][b, h], "q")[None, None]
+            k = as64(inp["k"][b, h // G], "k")[None, None]
+            v = as64(inp["v"][b, h // G], "v")[None, None]
+            oracle.attention(q, k, v, w.scale, w.causal)
+            heads += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    flop_per_head = w.flops() / (w.B * w.Hq)
+    value = flop_per_head * heads / elapsed / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same workload, full fp64 oracle, "
+                      f"{elapsed:.1f} s wall; FLOP counted causal-adjusted like the GPU value",
+            "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import sdpa_inputs
+    import scaled_dot_product_18_amd as sdpa
+    sdpa.require_library()
+
+    name = args.workload or sdpa_inputs.HEADLINE
+    w = sdpa_inputs.WORKLOADS[name]
+    log(f"[bench] workload {name}: generating inputs")
+    inp = sdpa_inputs.make_inputs(w)
+    dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
+    out = torch.empty((w.B, w.Hq, w.Sq, w.d), dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                      device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda") if w.want_lse else None
+
+    def step():
+        if w.dtype == "fp8":
+            sdpa.fwd_fp8(dev["q"], dev["k"], dev["v"], inp["descale_q"], inp["descale_k"], inp["descale_v"],
+                         causal=w.causal, scale=w.scale, out=out, lse_out=lse)
+        else:
+            sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, out=out, lse_out=lse)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    region_ms = region0.elapsed_time(region1)
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_launch_ms = sum(per_launch) / len(per_launch)
+    ms_per_step = region_ms / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, launch avg {avg_launch_ms * 1e3:.1f} us "
+        f"(median {per_launch[len(per_launch) // 2] * 1e3:.1f}, min {per_launch[0] * 1e3:.1f}), "
+        f"host wall {t_wall / args.steps * 1e3:.1f} us/step")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) q/k/v" + (", per-tensor amax e4m3fn" if w.dtype == "fp8" else ""),
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
+                   "causal": w.causal, "lse": w.want_lse, "in_dtype": w.dtype,
+                   "out_dtype": "f32" if w.dtype == "f32" else "bf16", "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "tokens_per_s": round(w.B * w.Sq / (ms_per_step * 1e-3), 1),
+        "hbm_gbs_algorithmic": round(w.hbm_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": kernel_name(w),
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic_from_profiles(w),
+            "algorithmic_flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": w.hbm_bytes(),
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+        },
+        "cpu_baseline": None,
+        "kernel_source_sha": kernel_source_hash(),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on a bounded sample ({args.cpu_budget:.0f} s budget)")
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,117 @@
+/*
+ * attn.h -- C ABI of the fused scaled dot-product attention forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (codelab "Accelerate attention on GPU with cuDNN and
+ * TransformerEngine", intro "How attention works" and section 4; article
+ * "Self-attention, CUDA kernels and FlashAttention", sections 1 and 3):
+ *
+ *   O[b,h,i,:] = sum_j softmax_j( scale * Q[b,h,i,:] . K[b,hk,j,:] ) * V[b,hk,j,:]
+ *   lse[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,hk,j,:] )
+ *
+ * over the allowed keys j: all of [0, Sk), or j <= i with the causal
+ * (lower-triangular) mask of the codelab's section 7. Query head h reads KV
+ * head hk = h / (Hq / Hkv): consecutive groups of query heads share one KV
+ * head (MHA when Hkv == Hq, GQA, MQA when Hkv == 1; codelab section 9).
+ * The computation is fused in the FlashAttention manner (article section 3):
+ * score tiles live only on chip, so no Sq x Sk matrix is written to memory;
+ * lse is the small per-row statistic that manner keeps for a backward pass.
+ *
+ * Layouts (all dense, row-major, no strides):
+ *   q, o  : [B, Hq,  Sq, d]
+ *   k, v  : [B, Hkv, Sk, d]
+ *   lse   : [B, Hq,  Sq] float32, natural-log units (may be NULL)
+ *
+ * Ownership and execution:
+ *   - every pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates no memory, keeps no state, and is safe to call from several
+ *     host threads;
+ *   - work is enqueued on `stream` (NULL = the null stream) and the call
+ *     returns without waiting; errors of the kernel itself surface on the
+ *     stream, as for any HIP launch;
+ *   - every element of o (and of lse when non-NULL) is written;
+ *   - outputs must not overlap inputs; base pointers must be 16-byte aligned.
+ *
+ * Errors are returned, never hidden: an unsupported request is rejected
+ * before anything is enqueued and nothing falls back to another path
+ * (the codelab's section 6 makes the same choice for its fused backend).
+ */
+#ifndef SDPA18_ATTN_H
+#define SDPA18_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v. Output o is f32 for ATTN_F32 and bf16 otherwise. */
+typedef enum {
+  ATTN_F32 = 0,      /* IEEE binary32 in, binary32 out                          */
+  ATTN_BF16 = 1,     /* bfloat16 in, bfloat16 out (RNE)                          */
+  ATTN_FP8_E4M3 = 2  /* OCP fp8 e4m3fn codes in (unit descales), bfloat16 out    */
+} attn_dtype_t;
+
+/* Status codes: 0 is success, every error is negative. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,          /* q, k, v or o is NULL                                  */
+  ATTN_ERR_SHAPE = -2,         /* a size is < 1, or the problem exceeds 32-bit indexing */
+  ATTN_ERR_HEADS = -3,         /* Hq is not a multiple of Hkv                           */
+  ATTN_ERR_HEADDIM = -4,       /* d is not 64 or 128                                    */
+  ATTN_ERR_CAUSAL_SHAPE = -5,  /* causal requested with Sq != Sk                        */
+  ATTN_ERR_DTYPE = -6,         /* dtype is not an attn_dtype_t value                    */
+  ATTN_ERR_SCALE = -7,         /* scale or a descale is not finite and > 0              */
+  ATTN_ERR_ALIGN = -8,         /* a base pointer is not 16-byte aligned                 */
+  ATTN_ERR_LAUNCH = -9         /* the HIP runtime rejected the kernel launch            */
+};
+
+/*
+ * attn_fwd -- fused attention forward.
+ *
+ *   q, k, v  device inputs of element type `dtype`, layouts above.
+ *   o        device output: float32 for ATTN_F32, bfloat16 otherwise.
+ *   lse      device float32 [B, Hq, Sq] or NULL to skip the statistic.
+ *   B, Hq, Hkv, Sq, Sk, d   sizes; Hq % Hkv == 0; d in {64, 128};
+ *            causal requires Sq == Sk (self-attention, codelab section 7).
+ *   scale    multiplier of the dot products, finite and > 0 (the pages use
+ *            1/sqrt(d)).
+ *   causal   0 = every key visible; nonzero = key j visible to query i iff j <= i.
+ *   dtype    attn_dtype_t; ATTN_FP8_E4M3 here means all descales are 1.
+ *   stream   HIP stream to enqueue on.
+ *
+ * Returns ATTN_OK or a negative status (see above).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d,
+             float scale, int causal, int dtype, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8 -- fused attention forward on fp8 e4m3fn inputs with
+ * per-tensor scales (codelab section 10: E4M3 forward format, per-tensor amax
+ * scaling). The real value of an input element is code * descale_x, with
+ * descale_x = amax(|x|) / 448 for per-tensor amax quantisation. Q.K^T runs on
+ * fp8 matrix cores with fp32 accumulation; the descales of Q and K fold into
+ * the softmax scale and descale_v into the epilogue.
+ *
+ *   q8, k8, v8  device uint8 e4m3fn codes, layouts as attn_fwd.
+ *   o_bf16      device bfloat16 output [B, Hq, Sq, d].
+ *   lse         as attn_fwd (of the dequantised scores), or NULL.
+ *   descale_q, descale_k, descale_v  finite and > 0.
+ *   Other arguments and the return value as attn_fwd.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/* attn_strerror -- static, NUL-terminated text for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* attn_version -- ABI version of this library (major * 10000 + minor * 100 + patch). */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA18_ATTN_H */

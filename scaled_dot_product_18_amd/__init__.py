@@ -1,0 +1,113 @@
+"""Fused scaled dot-product attention forward for AMD Instinct MI355X (gfx950).
+
+    o, lse = fwd(q, k, v, causal=True, want_lse=True)
+
+computes softmax(scale * Q K^T [+ causal mask]) V in one fused HIP kernel
+(codelab "Accelerate attention on GPU with cuDNN and TransformerEngine",
+intro and sections 4, 7, 9; article "Self-attention, CUDA kernels and
+FlashAttention", section 3). Tensors are [B, H, S, d] on the GPU; K and V may
+have fewer heads than Q (GQA/MQA, query head h reads KV head h // (Hq/Hkv)).
+
+This module only marshals arguments into the C ABI of libsdpa18.so
+(include/attn.h); PyTorch supplies device memory and the current stream.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import AttnError, ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3  # noqa: F401
+
+__all__ = ["fwd", "fwd_fp8", "AttnError", "library_path", "version", "require_library"]
+
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def version() -> int:
+    return _lib.load().attn_version()
+
+
+def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, d]")
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"q {tuple(q.shape)} does not match k {tuple(k.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise ValueError("inputs must be GPU tensors")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous [B, H, S, d]")
+        if t.device != q.device:
+            raise ValueError("inputs must be on one device")
+    return B, Hq, Hkv, Sq, Sk, d
+
+
+def _outputs(q, B, Hq, Sq, d, out_dtype, want_lse, out, lse_out):
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, Hq, Sq, d) or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    lse = None
+    if want_lse or lse_out is not None:
+        lse = lse_out if lse_out is not None else torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse_out must be a contiguous float32 [B, Hq, Sq] tensor")
+    return out, lse
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
+        want_lse: bool = False, out: Optional[torch.Tensor] = None,
+        lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused attention forward for float32 or bfloat16 inputs.
+
+    scale defaults to 1/sqrt(d). Returns (o, lse) with o in the input dtype and
+    lse float32 [B, Hq, Sq] (natural log) or None. Enqueued on the current
+    stream; nothing waits.
+    """
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"fwd takes float32 or bfloat16 q/k/v of one dtype, got {q.dtype}/{k.dtype}/{v.dtype}")
+    B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, B, Hq, Sq, d, q.dtype, want_lse, out, lse_out)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _lib.check(_lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             B, Hq, Hkv, Sq, Sk, d, scale, causal, _DTYPES[q.dtype], stream))
+    return out, lse
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: float, descale_k: float,
+            descale_v: float, *, causal: bool = False, scale: Optional[float] = None, want_lse: bool = False,
+            out: Optional[torch.Tensor] = None,
+            lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused attention forward on fp8-e4m3fn codes (uint8 or float8_e4m3fn tensors)
+    with per-tensor descales; bfloat16 output. Other arguments as :func:`fwd`."""
+    ok = (torch.uint8, torch.float8_e4m3fn)
+    if q8.dtype not in ok or k8.dtype not in ok or v8.dtype not in ok:
+        raise ValueError("fwd_fp8 takes uint8 or float8_e4m3fn codes")
+    B, Hq, Hkv, Sq, Sk, d = _shapes(q8, k8, v8)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q8, B, Hq, Sq, d, torch.bfloat16, want_lse, out, lse_out)
+    stream = torch.cuda.current_stream(q8.device).cuda_stream
+    _lib.check(_lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, Sq, Sk, d, scale, causal,
+                                 float(descale_q), float(descale_k), float(descale_v), stream))
+    return out, lse
+
+
+def require_library() -> None:
+    """Load libsdpa18.so now; raises RuntimeError if it is missing (there is no other path)."""
+    _lib.load()

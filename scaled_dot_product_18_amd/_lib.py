@@ -1,0 +1,83 @@
+"""ctypes binding of libsdpa18.so (the C ABI declared in include/attn.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's
+kernels. There is no fallback: a missing library or a rejected call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_NAME = "libsdpa18.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+
+STATUS = {
+    0: "ATTN_OK",
+    -1: "ATTN_ERR_NULL",
+    -2: "ATTN_ERR_SHAPE",
+    -3: "ATTN_ERR_HEADS",
+    -4: "ATTN_ERR_HEADDIM",
+    -5: "ATTN_ERR_CAUSAL_SHAPE",
+    -6: "ATTN_ERR_DTYPE",
+    -7: "ATTN_ERR_SCALE",
+    -8: "ATTN_ERR_ALIGN",
+    -9: "ATTN_ERR_LAUNCH",
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A status code other than ATTN_OK returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m scaled_dot_product_18_amd.build` "
+                               "(or __graft_entry__.build()); there is no non-HIP fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+        lib.attn_fwd.restype = i
+        lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
+        lib.attn_fwd_fp8.restype = i
+        lib.attn_strerror.argtypes = [i]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        lib.attn_version.argtypes = []
+        lib.attn_version.restype = i
+        _lib = lib
+        return lib
+
+
+def strerror(status: int) -> str:
+    return load().attn_strerror(int(status)).decode()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, strerror(status))
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dtype, stream)
+
+
+def attn_fwd_fp8(q8, k8, v8, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dq, dk, dv, stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_fwd_fp8(q8, k8, v8, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dq, dk, dv, stream)

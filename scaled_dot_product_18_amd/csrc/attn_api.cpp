@@ -1,0 +1,113 @@
+// C ABI of the fused attention library: argument validation and dispatch.
+//
+// Every check runs on the host before anything is enqueued, so a rejected
+// call has no effect on the stream. Unsupported requests are errors; there is
+// no fallback path.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* ptr) { return ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
+
+// Shared validation of attn_fwd and attn_fwd_fp8. Returns ATTN_OK or an error.
+int validate(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int Hq, int Hkv,
+             int Sq, int Sk, int d, int causal) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
+  // Row offsets inside one head and the grid size are 32-bit.
+  const int64_t block_m = 128;
+  const int64_t tiles = (Sq + block_m - 1) / block_m;
+  if ((int64_t)Sq * d * 4 >= INT32_MAX || (int64_t)Sk * d * 4 >= INT32_MAX ||
+      tiles * (int64_t)B * (int64_t)Hq >= INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (causal && Sq != Sk) return ATTN_ERR_CAUSAL_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int Sq, int Sk, float qk_scale, float o_scale, int block_m) {
+  sdpa18::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.group = Hq / Hkv;
+  p.n_qtiles = (Sq + block_m - 1) / block_m;
+  p.qk_scale_log2 = qk_scale * kLog2e;
+  p.o_scale = o_scale;
+  return p;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
+             int Sk, int d, float scale, int causal, int dtype, hipStream_t stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
+  if (dtype == ATTN_F32) {
+    const sdpa18::AttnParams p =
+        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::f32_block_m());
+    return launch_status(sdpa18::launch_attn_f32(p, d, causal != 0, stream));
+  }
+  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::mfma_block_m());
+  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, dtype == ATTN_FP8_E4M3, stream));
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int B, int Hq, int Hkv,
+                 int Sq, int Sk, int d, float scale, int causal, float descale_q, float descale_k, float descale_v,
+                 hipStream_t stream) {
+  const int st = validate(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  if (!positive_finite(scale) || !positive_finite(descale_q) || !positive_finite(descale_k) ||
+      !positive_finite(descale_v))
+    return ATTN_ERR_SCALE;
+  const float qk = scale * descale_q * descale_k;
+  if (!positive_finite(qk * kLog2e)) return ATTN_ERR_SCALE;
+  const sdpa18::AttnParams p =
+      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, qk, descale_v, sdpa18::mfma_block_m());
+  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, true, stream));
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "q, k, v or o is a null pointer";
+    case ATTN_ERR_SHAPE: return "a size is < 1 or the problem exceeds 32-bit indexing";
+    case ATTN_ERR_HEADS: return "Hq is not a multiple of Hkv";
+    case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal masking requires Sq == Sk";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
+    case ATTN_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Fused scaled dot-product attention forward for gfx950 on fp32 matrix cores:
+// fp32 inputs, fp32 products and accumulation, fp32 output. This is the
+// full-precision member of the kernel family; it uses the same transposed
+// formulation as the bf16/fp8 kernel (S^T = K . Q^T and O^T += V^T . P^T on
+// v_mfma_f32_32x32x2_f32, one query column per lane, online softmax as in
+// "Self-attention, CUDA kernels and FlashAttention", section 3) with P kept
+// in fp32. With a K depth of 2 per MFMA no operand needs transposing: the
+// A operand of P.V is one element of a V row per lane.
+//
+// One workgroup = 4 waves = 128 query rows of one (batch, query head); KV
+// tiles of 32 keys go through one LDS buffer (K rows padded by one float so
+// the column reads of the S^T operand hit distinct banks).
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace sdpa18 {
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void attn_fwd_f32_kernel(const AttnParams p) {
+  constexpr int BM = 128;
+  constexpr int BN = 32;
+  constexpr int KLD = D + 1;  // padded K row (floats)
+  constexpr int DB = D / 32;
+  constexpr int LOADS = BN * D / 4 / 256;  // float4 loads per thread per tensor per tile
+  __shared__ float ks[BN * KLD];
+  __shared__ __attribute__((aligned(16))) float vs[BN * D];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int BH = p.B * p.Hq;
+  const int seq = blockIdx.x / BH;
+  const int rem = blockIdx.x - seq * BH;
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - seq) : seq;
+  const int b = rem / p.Hq;
+  const int hq = rem - b * p.Hq;
+  const int hk = hq / p.group;
+
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + i32;
+
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+  const float* qbase = (const float*)p.q + qo_row0 * D;
+  const float* kbase = (const float*)p.k + kv_row0 * D;
+  const float* vbase = (const float*)p.v + kv_row0 * D;
+
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const bool wave_active = qw < p.Sq;
+  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
+
+  // Q fragment (B operand of S^T): step s, half g holds dim 2s + g.
+  float qf[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; ++s) qf[s] = (qi < p.Sq) ? qbase[(size_t)qi * D + 2 * s + g] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c = p.qk_scale_log2;
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int kv0 = kt * BN;
+    __syncthreads();  // previous tile fully consumed
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) {
+      const int f = tid + 256 * t;
+      const int row = f / (D / 4);
+      const int c4 = f - row * (D / 4);
+      const int kr = kv0 + row;
+      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      if (kr < p.Sk) {
+        kx = *(const float4*)(kbase + (size_t)kr * D + 4 * c4);
+        vx = *(const float4*)(vbase + (size_t)kr * D + 4 * c4);
+      }
+      float* kd = ks + row * KLD + 4 * c4;
+      kd[0] = kx.x;
+      kd[1] = kx.y;
+      kd[2] = kx.z;
+      kd[3] = kx.w;
+      *(float4*)(vs + row * D + 4 * c4) = vx;
+    }
+    __syncthreads();
+    if (kt >= wave_tiles) continue;
+
+    // S^T = K . Q^T: row i = key kv0 + i, column = query of this lane.
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 2; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[i32 * KLD + 2 * st + g], qf[st], s, 0, 0, 0);
+
+    // register r on half g holds key kv0 + 8(r/4) + 4g + (r%4)
+    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw) || (kv0 + BN > p.Sk);
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi);
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = halfwave_max(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = exp2_fast(m_run - m_new);
+    m_run = m_new;
+    float pr[16];
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pr[r] = exp2_fast(__builtin_fmaf(s[r], c, -m_new));
+      rs += pr[r];
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+
+    // O^T += V^T . P^T, one pair of keys per MFMA: step r takes key
+    // 8(r/4) + 4g + (r%4) from half g, matching the score registers.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * g + (r & 3);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * D + 32 * db + i32], pr[r], acc[db], 0, 0, 0);
+      }
+  }
+
+  if (!wave_active) return;
+  const float l_tot = halfwave_sum(l_run);
+  if (qi >= p.Sq) return;
+  const float inv = 1.0f / l_tot;
+  float* orow = (float*)p.o + (qo_row0 + qi) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;
+      *(float4*)(orow + d) = make_float4(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv,
+                                         acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv);
+    }
+  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  // hipLaunchKernel reports the status of this launch alone.
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel((const void*)&attn_fwd_f32_kernel<D, CAUSAL>, dim3(grid), dim3(256), args, 0, stream);
+}
+
+int f32_block_m() { return 128; }
+
+hipError_t launch_attn_f32(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+  return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+}
+
+}  // namespace sdpa18

@@ -1,0 +1,21 @@
+// Host-side entry points of the kernel translation units (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernel_common.h"
+
+namespace sdpa18 {
+
+// Query rows per workgroup of each kernel family (the grid is
+// ceil(Sq / block_m) x B x Hq workgroups).
+int mfma_block_m();
+int f32_block_m();
+
+// bf16 (fp8 = false) or fp8-e4m3fn (fp8 = true) inputs, bf16 output; d in {64, 128}.
+hipError_t launch_attn_mfma(const AttnParams& p, int d, bool causal, bool fp8, hipStream_t stream);
+
+// fp32 inputs and output; d in {64, 128}.
+hipError_t launch_attn_f32(const AttnParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace sdpa18

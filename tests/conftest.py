@@ -25,5 +25,6 @@ def gpu():
     """Skip where no GPU exists; on a GPU machine a missing library is a failure, not a skip."""
     if not gpu_available():
         pytest.skip("no GPU in this environment")
-    import scaled_dot_product_18_amd as sdpa  # raises if the built library is missing
+    import scaled_dot_product_18_amd as sdpa
+    sdpa.require_library()  # raises if the built library is missing
     return sdpa

@@ -1,0 +1,216 @@
+"""GPU parity of the fused HIP kernels against the fp64 oracle, through the C ABI.
+
+Small problems (spanning several tiles and a ragged tail) are compared element
+by element with the full oracle; the full-size workloads are launched exactly
+as the benchmark launches them and compared on sampled rows, which the oracle
+computes one by one. Tolerances are max |GPU - oracle|: 1e-4 fp32, 2e-2 bf16,
+6e-2 fp8 (on dequantised inputs); lse 1e-4 / 1e-3 / 1e-2.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sdpa_inputs
+from golden_io import load_all
+from parity_util import TOL_O, check_full, check_sampled, log, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+TAIL_S = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 196, 255, 257]
+HEADS = [(8, 8), (8, 2), (8, 1)]
+
+
+def _run_full(w, want_lse=True):
+    log(f"[parity] {w.name}")
+    inp = sdpa_inputs.make_inputs(w)
+    o, lse = run_gpu(w, to_device(inp), want_lse=want_lse)
+    torch.cuda.synchronize()
+    return check_full(w, inp, o, lse)
+
+
+# ------------------------------------------------------------ the small workloads
+
+def test_single_head_f32_workload(gpu):
+    stats = _run_full(sdpa_inputs.WORKLOADS["single_head_f32_s128_d64"])
+    log(f"  {stats}")
+
+
+def test_vit_b16_bf16_workload(gpu):
+    stats = _run_full(sdpa_inputs.WORKLOADS["vit_b16_bf16_b32_h12_s196_d64"])
+    log(f"  {stats}")
+
+
+# ------------------------------------------------------- tails, heads, causal
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product(TAIL_S, (64, 128), (False, True), HEADS)))
+def test_bf16_tails(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    w = sdpa_inputs.custom(1, Hq, Hkv, S, S, d, "bf16", causal, seed=1000 + S)
+    _run_full(w)
+
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (64, 128),
+                                                                    (False, True), [(4, 4), (4, 2), (4, 1)])))
+def test_f32_tails(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    _run_full(sdpa_inputs.custom(2, Hq, Hkv, S, S, d, "f32", causal, seed=2000 + S))
+
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 63, 64, 65, 129, 257], (64, 128),
+                                                                    (False, True), HEADS)))
+def test_fp8_tails(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    _run_full(sdpa_inputs.custom(1, Hq, Hkv, S, S, d, "fp8", causal, seed=3000 + S))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("Sq,Sk", [(1, 300), (77, 5), (130, 257), (300, 64)])
+def test_cross_attention_lengths(gpu, dtype, Sq, Sk):
+    """Unmasked attention with Sq != Sk (query and key sequences of different length)."""
+    _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, 128 if dtype != "f32" else 64, dtype, False, seed=Sq * 7 + Sk))
+
+
+def test_batch_and_heads_mapping(gpu):
+    """Several batches and GQA groups at once, causal, lse on."""
+    for dtype in ("f32", "bf16", "fp8"):
+        _run_full(sdpa_inputs.custom(3, 12, 3, 200, 200, 64, dtype, True, seed=55))
+
+
+# ------------------------------------------------------------- golden fixtures
+
+def test_golden_fixtures_fp32(gpu):
+    """The hand-derived fixtures, zero-padded to d = 64 (padding leaves every dot product
+    and the first output columns unchanged)."""
+    import scaled_dot_product_18_amd as sdpa
+    for c in load_all():
+        log(f"[golden] {c['name']}")
+        q, k, v = c["q"], c["k"], c["v"]
+        d0 = q.shape[-1]
+
+        def pad(x):
+            y = np.zeros(x.shape[:-1] + (64,))
+            y[..., :d0] = x
+            return torch.from_numpy(y).to(torch.float32).cuda().contiguous()
+
+        o, lse = sdpa.fwd(pad(q), pad(k), pad(v), causal=c["causal"], scale=c["scale"], want_lse=True)
+        torch.cuda.synchronize()
+        o = o.double().cpu().numpy()
+        np.testing.assert_allclose(o[..., :d0], c["o"], atol=1e-5)
+        np.testing.assert_array_equal(o[..., d0:], 0.0)
+        np.testing.assert_allclose(lse.double().cpu().numpy(), c["lse"], atol=1e-5)
+
+
+# ----------------------------------------------------------------- properties
+
+def test_large_score_offset(gpu):
+    """Scores around 1e3: the online softmax stays finite and matches the oracle."""
+    import scaled_dot_product_18_amd as sdpa
+    g = torch.Generator().manual_seed(5)
+    S, d = 150, 64
+    base = torch.full((1, 2, S, d), 4.0)
+    q = (base + 0.1 * torch.randn(1, 2, S, d, generator=g)).to(torch.bfloat16)
+    k = (base + 0.1 * torch.randn(1, 2, S, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(1, 2, S, d, generator=g).to(torch.bfloat16)
+    for causal in (False, True):
+        o, lse = sdpa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=1.0, want_lse=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 1.0, causal)
+        assert np.all(l_ref > 900)
+        assert np.abs(o.double().cpu().numpy() - o_ref).max() <= TOL_O["bf16"]
+        assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= 1e-5 * 1000 + 1e-3
+
+
+def test_every_output_written(gpu):
+    """Outputs pre-filled with NaN are overwritten everywhere (tails included)."""
+    for dtype in ("f32", "bf16", "fp8"):
+        w = sdpa_inputs.custom(2, 4, 2, 131, 131, 128, dtype, True, seed=9)
+        dev = to_device(sdpa_inputs.make_inputs(w))
+        out = torch.full((2, 4, 131, 128), float("nan"), dtype=torch.float32 if dtype == "f32" else torch.bfloat16,
+                         device="cuda")
+        lse = torch.full((2, 4, 131), float("nan"), device="cuda")
+        run_gpu(w, dev, out=out, lse_out=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_deterministic(gpu):
+    """Bitwise identical results across repeated calls (no atomics, fixed reduction order)."""
+    w = sdpa_inputs.custom(2, 8, 2, 517, 517, 128, "bf16", True, seed=11)
+    dev = to_device(sdpa_inputs.make_inputs(w))
+    o1, l1 = run_gpu(w, dev)
+    o2, l2 = run_gpu(w, dev)
+    for _ in range(3):
+        o3, l3 = run_gpu(w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l2) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_gqa_equals_mha_on_repeated_kv(gpu, dtype):
+    """GQA/MQA output is bit-identical to MHA on host-repeated K/V heads."""
+    for Hkv in (2, 1):
+        w = sdpa_inputs.custom(2, 8, Hkv, 190, 190, 64, dtype, True, seed=21)
+        inp = sdpa_inputs.make_inputs(w)
+        o_g, l_g = run_gpu(w, to_device(inp))
+        G = 8 // Hkv
+        rep = dict(inp, k=inp["k"].repeat_interleave(G, dim=1).contiguous(),
+                   v=inp["v"].repeat_interleave(G, dim=1).contiguous())
+        w_m = sdpa_inputs.custom(2, 8, 8, 190, 190, 64, dtype, True, seed=21)
+        o_m, l_m = run_gpu(w_m, to_device(rep))
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_m) and torch.equal(l_g, l_m)
+
+
+def test_causal_first_row_is_v0(gpu):
+    """Causal row 0 attends only to key 0: O[...,0,:] = V[...,0,:] exactly, lse = scale q0.k0."""
+    w = sdpa_inputs.custom(2, 4, 4, 300, 300, 128, "bf16", True, seed=31)
+    inp = sdpa_inputs.make_inputs(w)
+    o, lse = run_gpu(w, to_device(inp))
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0].cpu(), inp["v"][:, :, 0])
+    s0 = (inp["q"][:, :, 0].double() * inp["k"][:, :, 0].double()).sum(-1) * w.scale
+    assert torch.allclose(lse[:, :, 0].cpu().double(), s0, atol=1e-4)
+
+
+def test_lse_optional(gpu):
+    w = sdpa_inputs.custom(1, 4, 4, 100, 100, 64, "bf16", False, seed=41)
+    dev = to_device(sdpa_inputs.make_inputs(w))
+    o1, lse = run_gpu(w, dev, want_lse=False)
+    o2, _ = run_gpu(w, dev, want_lse=True)
+    torch.cuda.synchronize()
+    assert lse is None and torch.equal(o1, o2)
+
+
+def test_errors_raise_through_python(gpu):
+    import scaled_dot_product_18_amd as sdpa
+    x = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.AttnError, match="ATTN_ERR_HEADS"):
+        sdpa.fwd(x, kv, kv)
+    y = torch.zeros(1, 2, 8, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.AttnError, match="ATTN_ERR_HEADDIM"):
+        sdpa.fwd(y, y, y)
+    z = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    z9 = torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.AttnError, match="ATTN_ERR_CAUSAL_SHAPE"):
+        sdpa.fwd(z, z9, z9, causal=True)
+
+
+# ----------------------------------------------- full-size workloads, sampled rows
+
+@pytest.mark.parametrize("name", ["causal_mha_bf16_b8_h16_s2048_d128", "causal_gqa_bf16_b4_hq32_hkv8_s4096_d128",
+                                  "causal_mqa_bf16_b4_hq32_hkv1_s4096_d128", "causal_fp8_b1_h32_s16384_d128"])
+def test_full_size_workload_sampled(gpu, name):
+    w = sdpa_inputs.WORKLOADS[name]
+    log(f"[parity-full] {name}")
+    inp = sdpa_inputs.make_inputs(w)
+    dev = to_device(inp)
+    o, lse = run_gpu(w, dev, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    stats = check_sampled(w, inp, o, lse, n_random=16 if w.Sq > 8192 else 24)
+    log(f"  {stats}")
