@@ -40,7 +40,7 @@ METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of MFMA peak, 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
-KERNEL_SOURCES = ["kernel_common.h", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+KERNEL_SOURCES = ["kernel_common.h", "attn_fwd_bf16.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
 
 
 def log(msg: str) -> None:
@@ -56,9 +56,7 @@ def kernel_source_hash() -> str:
 
 
 def kernel_name(w) -> str:
-    if w.dtype == "f32":
-        return "attn_fwd_f32_kernel"
-    return "attn_fwd_mfma_kernel"
+    return {"f32": "attn_fwd_f32_kernel", "bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_mfma_kernel"}[w.dtype]
 
 
 def traffic_from_profiles(w):

@@ -53,6 +53,8 @@ sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void
   p.n_qtiles = (Sq + block_m - 1) / block_m;
   p.qk_scale_log2 = qk_scale * kLog2e;
   p.o_scale = o_scale;
+  // Each XCD gets whole KV heads when they split evenly over the 8 XCDs.
+  p.xcd_remap = ((B * Hkv) % 8 == 0) ? 1 : 0;
   return p;
 }
 
@@ -73,8 +75,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
         make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::f32_block_m());
     return launch_status(sdpa18::launch_attn_f32(p, d, causal != 0, stream));
   }
+  if (dtype == ATTN_BF16) {
+    const sdpa18::AttnParams p =
+        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::bf16_block_m());
+    return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
+  }
   const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::mfma_block_m());
-  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, dtype == ATTN_FP8_E4M3, stream));
+  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, true, stream));
 }
 
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int B, int Hq, int Hkv,

@@ -1,0 +1,318 @@
+// Fused scaled dot-product attention forward for gfx950, bf16 inputs and output.
+//
+// The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
+// and FlashAttention", section 3): K and V stream through on-chip tiles, the
+// scores of a tile exist only in registers, a running row maximum and
+// normaliser rescale the partial output as tiles arrive (online softmax), and
+// only O and the per-row log-sum-exp are written. The arithmetic is the
+// codelab's three steps ("Accelerate attention on GPU with cuDNN and
+// TransformerEngine", intro and section 4) with the lower-triangular mask of
+// its section 7 and the shared KV heads of its section 9.
+//
+// Layout of the work on CDNA4:
+//  * one workgroup = 4 waves = 128 query rows of one (batch, query head);
+//    wave w owns rows [32w, 32w+32) and keeps their Q fragment in VGPRs;
+//  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16,
+//    so each lane owns one query column: row max / row sum are in-lane plus one
+//    v_permlane32_swap, and per-row factors are lane scalars;
+//  * the accumulator registers of S^T, rounded to bf16, are directly the B
+//    operand of O^T += V^T . P^T; the V^T operand comes from a row-major V tile
+//    through ds_read_b64_tr_b16 (4 consecutive keys at one dimension per read);
+//  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no staging
+//    registers), double buffered, one barrier per tile; both tiles carry an
+//    XOR swizzle of their 16-byte chunks that keeps the MFMA operand reads free
+//    of bank conflicts;
+//  * the running maximum is only moved (and O, l rescaled) when a tile's
+//    maximum exceeds it by more than 2^8 in probability units; otherwise the
+//    stale maximum is kept. Softmax is invariant to the reference point, so
+//    this is exact, and it removes the per-tile rescale of the accumulator;
+//  * row sums are taken with v_dot2_f32_bf16 on the bf16 probabilities the
+//    MFMA consumes, so numerator and normaliser use the same values;
+//  * causal workgroups stop at the diagonal, run heaviest first, and query
+//    heads that share a KV head are placed on the same XCD (same L2).
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace sdpa18 {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(1))) const void global_cvoid;
+
+template <int D>
+struct Bf16Cfg {
+  static constexpr int BM = 128;             // query rows per workgroup
+  static constexpr int BN = 8192 / D;        // keys per tile: 64 (d=128), 128 (d=64)
+  static constexpr int RB = D * 2;           // bytes per K/V row
+  static constexpr int CH = RB / 16;         // 16-byte chunks per row
+  static constexpr int TILE = BN * RB;       // bytes of a K (or V) tile: 16 KB
+  static constexpr int STAGE = 2 * TILE;     // K tile then V tile
+  static constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide DMA instructions per tensor per wave
+  static constexpr int ROWS_PER_DMA = 1024 / RB;
+  static constexpr int KB = BN / 32;         // 32-key blocks of a score tile
+  static constexpr int KC = BN / 16;         // 16-key chunks (K depth of P.V)
+  static constexpr int DB = D / 32;          // 32-wide output blocks
+  static constexpr int QS = D / 16;          // MFMAs per 32x32 score block
+  static_assert(DMA == 4, "4 waves x 4 DMA instructions cover a 16 KB tile");
+};
+
+// Chunk swizzle of K rows: lanes 0..15 of an operand read hit 16 different rows
+// at one logical chunk; XOR with a row-dependent value spreads them over all banks.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+// Chunk swizzle of V rows: a 16-lane transposing read touches 4 consecutive rows
+// at 32 consecutive bytes; the XOR values {0,6,10,12} (d=128) / {0,2,4,6} (d=64)
+// place the 4 rows on disjoint banks for both 32- and 64-bank LDS.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) {
+  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
+}
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unless exceeded by 2^8
+
+__device__ __forceinline__ void dma16(const unsigned char* gsrc, unsigned char* ldst) {
+  __builtin_amdgcn_global_load_lds((global_cvoid*)gsrc, (lds_void*)ldst, 16, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void attn_fwd_bf16_kernel(const AttnParams p) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and LDS bases
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+
+  // ---- work item: (q-tile, batch, query head) ------------------------------
+  int qt_seq, b, hq;
+  if (p.xcd_remap) {
+    // Workgroup i runs on XCD i % 8. Give each XCD whole KV heads (all query
+    // heads of a group), q-tiles outermost so every XCD starts on the heaviest.
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;
+    const int per_qt = (p.B * p.Hkv / 8) * p.group;
+    qt_seq = j / per_qt;
+    const int rem = j - qt_seq * per_qt;
+    const int pair = (rem / p.group) * 8 + xcd;
+    const int gq = rem - (rem / p.group) * p.group;
+    b = pair / p.Hkv;
+    hq = (pair - b * p.Hkv) * p.group + gq;
+  } else {
+    const int BH = p.B * p.Hq;
+    qt_seq = blockIdx.x / BH;
+    const int rem = blockIdx.x - qt_seq * BH;
+    b = rem / p.Hq;
+    hq = rem - b * p.Hq;
+  }
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_seq) : qt_seq;
+  const int hk = hq / p.group;
+
+  const int q0 = qt * C::BM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + i32;
+
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
+  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::RB;
+  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * C::RB;
+
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM) : p.Sk;
+  const int n_tiles = (kv_end + C::BN - 1) / C::BN;
+  const bool wave_active = qw < p.Sq;
+  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / C::BN + 1) : n_tiles);
+
+  // ---- DMA assignment: wave w writes 1 KB blocks 4w..4w+3 of each tile -----
+  // 16-byte slot s = 64*(4w+t) + lane holds row s / CH, physical chunk s % CH.
+  unsigned kdma_off[C::DMA], vdma_off[C::DMA];  // unsigned: SGPR base + 32-bit VGPR offset addressing
+  int dma_row[C::DMA];
+  const int dma_pchunk = lane % C::CH;
+#pragma unroll
+  for (int t = 0; t < C::DMA; ++t) {
+    const int row = (64 * (4 * wave + t) + lane) / C::CH;
+    dma_row[t] = row;
+    kdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ k_swizzle<D>(row));
+    vdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ v_swizzle<D>(row));
+  }
+
+  auto issue_tile = [&](int kt, unsigned char* stage) {
+    const int kv0 = kt * C::BN;
+    const unsigned char* kt_base = kbase + (size_t)kv0 * C::RB;
+    const unsigned char* vt_base = vbase + (size_t)kv0 * C::RB;
+    unsigned char* kdst = stage + 1024 * 4 * wave;
+    unsigned char* vdst = stage + C::TILE + 1024 * 4 * wave;
+    if (kv0 + C::BN <= p.Sk) {
+#pragma unroll
+      for (int t = 0; t < C::DMA; ++t) {
+        dma16(kt_base + kdma_off[t], kdst + 1024 * t);
+        dma16(vt_base + vdma_off[t], vdst + 1024 * t);
+      }
+    } else {
+      // tail tile: rows past Sk re-read row Sk-1 (finite data; those keys are
+      // masked to -inf, so their probabilities are exactly 0)
+#pragma unroll
+      for (int t = 0; t < C::DMA; ++t) {
+        const int shift = (min(kv0 + dma_row[t], p.Sk - 1) - kv0 - dma_row[t]) * C::RB;  // <= 0
+        dma16(kt_base + (ptrdiff_t)kdma_off[t] + shift, kdst + 1024 * t);
+        dma16(vt_base + (ptrdiff_t)vdma_off[t] + shift, vdst + 1024 * t);
+      }
+    }
+  };
+
+  // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
+  u32x4 qf[C::QS];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s)
+    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * C::RB + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+
+  // ---- per-lane LDS operand offsets ------------------------------------------
+  // K (A operand of S^T): row 32kb + i32, logical chunk 2s + g.
+  int k_rd[C::QS];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) k_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ k_swizzle<D>(i32));
+  // V (A operand of O^T through the transposing read): in each 16-lane group,
+  // lane J reads 4 dims [dbase + 4(J%4), +4) of key row (row_base + J/4).
+  const int J = lane & 15;
+  int v_rd[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int row = 4 * g + (J >> 2);
+    const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
+    v_rd[db] = row * C::RB + 16 * ((d >> 3) ^ v_swizzle<D>(row)) + 2 * (d & 7);
+  }
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY;  // reference maximum, log2 units of the scaled score
+  float l_run = 0.f;        // this lane's share of the normaliser
+  const float c = p.qk_scale_log2;
+  typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(bf16_t)1.0f, (bf16_t)1.0f};
+
+  auto compute_tile = [&](int kt, const unsigned char* stage) {
+    const int kv0 = kt * C::BN;
+    const unsigned char* kl = stage;
+    const unsigned char* vl = stage + C::TILE;
+
+    // S^T = K . Q^T
+    f32x16 s[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st) {
+        const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+      }
+    }
+
+    // register r of block kb on half g holds key kv0 + 32kb + 8(r/4) + 4g + r%4
+    if ((CAUSAL && kv0 + C::BN - 1 > qw) || kv0 + C::BN > p.Sk) {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi);
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+        }
+    }
+
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float m_tile = halfwave_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+    }
+
+    // P^T operand: chunk kc = 2kb + j, element e <-> key 16kc + 8(e/4) + 4g + e%4
+    u32x4 pf[C::KC];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 8 * j + 2 * e2;
+          const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_run));
+          const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_run));
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pf[2 * kb + j][e2] = w;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+        }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc) * C::RB + v_rd[db]));
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc + 8) * C::RB + v_rd[db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
+      }
+  };
+
+  // ---- main loop: DMA of tile kt+1 overlaps compute of tile kt --------------
+  if (n_tiles > 0) issue_tile(0, smem);
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    if (kt + 1 < n_tiles) issue_tile(kt + 1, smem + C::STAGE);
+    if (kt < wave_tiles) compute_tile(kt, smem);
+    __syncthreads();
+    if (kt + 1 >= n_tiles) break;
+    if (kt + 2 < n_tiles) issue_tile(kt + 2, smem);
+    if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem + C::STAGE);
+    __syncthreads();
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  if (!wave_active) return;
+  const float l_tot = halfwave_sum(l_run);
+  if (qi >= p.Sq) return;
+  const float inv = 1.0f / l_tot;
+  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)C::RB;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;  // registers 4q4..4q4+3 hold dims d..d+3
+      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+    }
+  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<D, CAUSAL>, dim3(grid), dim3(256), args, 0, stream);
+}
+
+int bf16_block_m() { return 128; }
+
+hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+  return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+}
+
+}  // namespace sdpa18

@@ -11,8 +11,12 @@ namespace sdpa18 {
 // ceil(Sq / block_m) x B x Hq workgroups).
 int mfma_block_m();
 int f32_block_m();
+int bf16_block_m();
 
-// bf16 (fp8 = false) or fp8-e4m3fn (fp8 = true) inputs, bf16 output; d in {64, 128}.
+// bf16 inputs and output; d in {64, 128}.
+hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream);
+
+// fp8-e4m3fn (fp8 = true) or bf16 inputs, bf16 output; d in {64, 128}.
 hipError_t launch_attn_mfma(const AttnParams& p, int d, bool causal, bool fp8, hipStream_t stream);
 
 // fp32 inputs and output; d in {64, 128}.

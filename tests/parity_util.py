@@ -12,9 +12,12 @@ import oracle
 from oracle import e4m3
 import sdpa_inputs
 
-# Tolerances: max |GPU - oracle| over every compared element.
+# Tolerances: max |GPU - oracle| over every compared element. O: fixed per dtype.
+# lse: the bf16 and fp8 kernels sum the bf16-rounded probabilities that the
+# P.V product consumes (relative error <= 2^-8 each), so their log-sum-exp can
+# be off by up to ln(1 + 2^-8) = 3.9e-3; the fp32 kernel keeps fp32 probabilities.
 TOL_O = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
-TOL_LSE = {"f32": 1e-4, "bf16": 1e-3, "fp8": 1e-2}
+TOL_LSE = {"f32": 1e-4, "bf16": 4e-3, "fp8": 1e-2}
 
 
 def log(msg: str) -> None:

@@ -4,7 +4,7 @@ Small problems (spanning several tiles and a ragged tail) are compared element
 by element with the full oracle; the full-size workloads are launched exactly
 as the benchmark launches them and compared on sampled rows, which the oracle
 computes one by one. Tolerances are max |GPU - oracle|: 1e-4 fp32, 2e-2 bf16,
-6e-2 fp8 (on dequantised inputs); lse 1e-4 / 1e-3 / 1e-2.
+6e-2 fp8 (on dequantised inputs); lse 1e-4 / 4e-3 / 1e-2.
 """
 
 import itertools
@@ -121,7 +121,7 @@ def test_large_score_offset(gpu):
         o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 1.0, causal)
         assert np.all(l_ref > 900)
         assert np.abs(o.double().cpu().numpy() - o_ref).max() <= TOL_O["bf16"]
-        assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= 1e-5 * 1000 + 1e-3
+        assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= 1e-5 * 1000 + 4e-3
 
 
 def test_every_output_written(gpu):
