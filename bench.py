@@ -40,7 +40,7 @@ METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of MFMA peak, 1 MI355X"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
-KERNEL_SOURCES = ["kernel_common.h", "attn_fwd_bf16.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+CSRC = os.path.join(ROOT, "scaled_dot_product_18_amd", "csrc")
 
 
 def log(msg: str) -> None:
@@ -48,10 +48,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """sha256 (16 hex digits) over every kernel and launch source: a counter
+    summary taken on other sources no longer describes the kernel."""
     h = hashlib.sha256()
-    for fn in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "scaled_dot_product_18_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(fn.encode())
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -60,18 +64,25 @@ def kernel_name(w) -> str:
 
 
 def traffic_from_profiles(w):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the current kernel."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.json")
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kernel>_<workload>_hbm.txt, or None when it is missing or was
+    taken on other kernel sources. The file holds 'key: value' lines; the
+    ones read here are kernel_source_sha and hbm_bytes_per_launch."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name(w)}_{w.name}_hbm.txt")
     if not os.path.exists(path):
         return None
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep:
+                rec[key.strip()] = val.strip()
     if rec.get("kernel_source_sha") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, inp, budget_s: float = 15.0) -> dict:
