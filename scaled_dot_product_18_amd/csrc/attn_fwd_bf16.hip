@@ -18,10 +18,14 @@
 //  * the accumulator registers of S^T, rounded to bf16, are directly the B
 //    operand of O^T += V^T . P^T; the V^T operand comes from a row-major V tile
 //    through ds_read_b64_tr_b16 (4 consecutive keys at one dimension per read);
-//  * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no staging
-//    registers), double buffered, one barrier per tile; both tiles carry an
-//    XOR swizzle of their 16-byte chunks that keeps the MFMA operand reads free
-//    of bank conflicts;
+//  * K and V tiles go HBM -> LDS with buffer_load_dwordx4 ... lds (no staging
+//    registers, no per-lane address arithmetic: the tile offset lives in the
+//    buffer descriptor), double buffered in two separate LDS objects so the
+//    compiler never makes a read of one stage wait for the loads into the
+//    other, one barrier per tile; rows past the end of the sequence fall
+//    outside the buffer's range and load as zeros; both tiles carry an XOR
+//    swizzle of their 16-byte chunks that keeps the MFMA operand reads free of
+//    bank conflicts;
 //  * the running maximum is only moved (and O, l rescaled) when a tile's
 //    maximum exceeds it by more than 2^8 in probability units; otherwise the
 //    stale maximum is kept. Softmax is invariant to the reference point, so
@@ -38,7 +42,6 @@ namespace sdpa18 {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(1))) const void global_cvoid;
 
 template <int D>
 struct Bf16Cfg {
@@ -73,15 +76,29 @@ __device__ __forceinline__ int v_swizzle(int row) {
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unless exceeded by 2^8
 
-__device__ __forceinline__ void dma16(const unsigned char* gsrc, unsigned char* ldst) {
-  __builtin_amdgcn_global_load_lds((global_cvoid*)gsrc, (lds_void*)ldst, 16, 0, 0);
+constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource: 32-bit data format (gfx9 family)
+
+// This wave's 4 wave-wide loads of one K or V tile, HBM -> LDS (lane l of load
+// t fills the 16 bytes at dst + 1024 t + 16 l). The tile is read through a raw
+// buffer that starts at its first row and ends at the end of the sequence, so
+// rows at or past Sk fall outside the buffer and load as zeros. Called from
+// the kernel body, not from a lambda: the host pass rejects a device function
+// called from a lambda in a kernel template and then drops the launch stub.
+__device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int seq_bytes,
+                                         const unsigned* off, unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + kt * tile_bytes), (short)0, seq_bytes - kt * tile_bytes, kBufferConfig);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
 }
 
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and LDS bases
@@ -130,40 +147,14 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
 
   // ---- DMA assignment: wave w writes 1 KB blocks 4w..4w+3 of each tile -----
   // 16-byte slot s = 64*(4w+t) + lane holds row s / CH, physical chunk s % CH.
-  unsigned kdma_off[C::DMA], vdma_off[C::DMA];  // unsigned: SGPR base + 32-bit VGPR offset addressing
-  int dma_row[C::DMA];
+  unsigned kdma_off[C::DMA], vdma_off[C::DMA];
   const int dma_pchunk = lane % C::CH;
 #pragma unroll
   for (int t = 0; t < C::DMA; ++t) {
     const int row = (64 * (4 * wave + t) + lane) / C::CH;
-    dma_row[t] = row;
     kdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ k_swizzle<D>(row));
     vdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ v_swizzle<D>(row));
   }
-
-  auto issue_tile = [&](int kt, unsigned char* stage) {
-    const int kv0 = kt * C::BN;
-    const unsigned char* kt_base = kbase + (size_t)kv0 * C::RB;
-    const unsigned char* vt_base = vbase + (size_t)kv0 * C::RB;
-    unsigned char* kdst = stage + 1024 * 4 * wave;
-    unsigned char* vdst = stage + C::TILE + 1024 * 4 * wave;
-    if (kv0 + C::BN <= p.Sk) {
-#pragma unroll
-      for (int t = 0; t < C::DMA; ++t) {
-        dma16(kt_base + kdma_off[t], kdst + 1024 * t);
-        dma16(vt_base + vdma_off[t], vdst + 1024 * t);
-      }
-    } else {
-      // tail tile: rows past Sk re-read row Sk-1 (finite data; those keys are
-      // masked to -inf, so their probabilities are exactly 0)
-#pragma unroll
-      for (int t = 0; t < C::DMA; ++t) {
-        const int shift = (min(kv0 + dma_row[t], p.Sk - 1) - kv0 - dma_row[t]) * C::RB;  // <= 0
-        dma16(kt_base + (ptrdiff_t)kdma_off[t] + shift, kdst + 1024 * t);
-        dma16(vt_base + (ptrdiff_t)vdma_off[t] + shift, vdst + 1024 * t);
-      }
-    }
-  };
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
   u32x4 qf[C::QS];
@@ -271,15 +262,25 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   };
 
   // ---- main loop: DMA of tile kt+1 overlaps compute of tile kt --------------
-  if (n_tiles > 0) issue_tile(0, smem);
+  const int kv_bytes = p.Sk * C::RB;
+  if (n_tiles > 0) {
+    dma_tile(kbase, C::TILE, 0, kv_bytes, kdma_off, smem0 + 4096 * wave);
+    dma_tile(vbase, C::TILE, 0, kv_bytes, vdma_off, smem0 + C::TILE + 4096 * wave);
+  }
   __syncthreads();
   for (int kt = 0; kt < n_tiles; kt += 2) {
-    if (kt + 1 < n_tiles) issue_tile(kt + 1, smem + C::STAGE);
-    if (kt < wave_tiles) compute_tile(kt, smem);
+    if (kt + 1 < n_tiles) {
+      dma_tile(kbase, C::TILE, kt + 1, kv_bytes, kdma_off, smem1 + 4096 * wave);
+      dma_tile(vbase, C::TILE, kt + 1, kv_bytes, vdma_off, smem1 + C::TILE + 4096 * wave);
+    }
+    if (kt < wave_tiles) compute_tile(kt, smem0);
     __syncthreads();
     if (kt + 1 >= n_tiles) break;
-    if (kt + 2 < n_tiles) issue_tile(kt + 2, smem);
-    if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem + C::STAGE);
+    if (kt + 2 < n_tiles) {
+      dma_tile(kbase, C::TILE, kt + 2, kv_bytes, kdma_off, smem0 + 4096 * wave);
+      dma_tile(vbase, C::TILE, kt + 2, kv_bytes, vdma_off, smem0 + C::TILE + 4096 * wave);
+    }
+    if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem1);
     __syncthreads();
   }
 
