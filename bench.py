@@ -60,6 +60,8 @@ def kernel_source_hash() -> str:
 
 
 def kernel_name(w) -> str:
+    if w.dtype == "bf16" and w.d == 128:
+        return "attn_fwd_bf16_pp_kernel"
     return {"f32": "attn_fwd_f32_kernel", "bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_mfma_kernel"}[w.dtype]
 
 

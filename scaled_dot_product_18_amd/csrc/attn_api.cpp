@@ -77,7 +77,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
   if (dtype == ATTN_BF16) {
     const sdpa18::AttnParams p =
-        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::bf16_block_m());
+        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::bf16_block_m(d));
     return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
   }
   const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::mfma_block_m());

@@ -10,6 +10,8 @@
 // its section 7 and the shared KV heads of its section 9.
 //
 // Layout of the work on CDNA4:
+//  * this four-wave kernel serves head dimension 64 (the eight-wave ping-pong
+//    kernel in attn_fwd_bf16_pp.hip serves 128);
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //    wave w owns rows [32w, 32w+32) and keeps their Q fragment in VGPRs;
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16,
@@ -309,10 +311,11 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<D, CAUSAL>, dim3(grid), dim3(256), args, 0, stream);
 }
 
-int bf16_block_m() { return 128; }
+int bf16_block_m(int d) { return d == 128 ? bf16_pp_block_m() : Bf16Cfg<64>::BM; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+  // d = 128: the eight-wave ping-pong kernel (attn_fwd_bf16_pp.hip); d = 64 here.
+  if (d == 128) return launch_attn_bf16_pp(p, causal, stream);
   return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }
 

@@ -1,0 +1,374 @@
+// Fused scaled dot-product attention forward for gfx950, bf16, head dim 128:
+// eight waves per workgroup in matrix-core / vector-unit ping-pong.
+//
+// The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
+// and FlashAttention", section 3): K and V stream through on-chip tiles, the
+// scores of a tile exist only in registers, a running row maximum and
+// normaliser rescale the partial output as tiles arrive (online softmax), and
+// only O and the per-row log-sum-exp are written. The arithmetic is the
+// codelab's three steps ("Accelerate attention on GPU with cuDNN and
+// TransformerEngine", intro and section 4) with the lower-triangular mask of
+// its section 7 and the shared KV heads of its section 9.
+//
+// Work of one wave (32 query rows) over its T key tiles of 64 keys is a chain
+// of phases  M0 V0 M1 V1 ... M(T-1) V(T-1) MT:
+//   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T   (32 MFMAs)
+//   V(m): mask, row max, lazy rescale, P(m) = exp2(S(m) c - m_ref), row sums
+// A workgroup holds 8 waves, two per SIMD: group A (waves 0-3) runs M phases
+// on even global phases and V phases on odd ones, group B (waves 4-7) the
+// other way round, so on every SIMD one wave feeds the matrix core while the
+// other keeps the vector unit busy. A workgroup barrier separates global
+// phases. The two waves of a SIMD own adjacent 32-row blocks, so they have the
+// same number of key tiles.
+//
+// K/V tiles: K(n+1) and V(n) are loaded HBM -> LDS (buffer_load ... lds, 2 KB
+// per wave) at the start of global phase 2n and waited for before the barrier
+// that ends phase 2n+1; K(m) is read in phases 2m (A) and 2m+1 (B), V(m-1)
+// likewise, so two K slots and two V slots suffice. The loop is unrolled over
+// four phases so that every slot is a fixed LDS object and the compiler can
+// see that a read never touches the slot being filled.
+//
+// Lane layout (unchanged from the four-wave kernel): S^T and O^T are computed
+// transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one query
+// column; the bf16-rounded score accumulator is directly the P^T operand; V^T
+// comes from the row-major V tile through ds_read_b64_tr_b16; XOR swizzles
+// keep the operand reads free of bank conflicts; the running maximum only
+// moves when a tile exceeds it by 2^8 (exact: softmax does not depend on the
+// reference point); row sums use v_dot2_f32_bf16 on the bf16 probabilities.
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace sdpa18 {
+namespace pp {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int WAVES = 8;
+constexpr int BM = 32 * WAVES;  // query rows per workgroup
+constexpr int BN = 64;          // keys per tile
+constexpr int RB = D * 2;       // bytes per K/V row
+constexpr int CH = RB / 16;     // 16-byte chunks per row
+constexpr int TILE = BN * RB;   // 16 KB
+constexpr int DMA = TILE / 1024 / WAVES;  // 1 KB wave-wide loads per tensor per wave
+constexpr int KB = BN / 32;     // 32-key blocks of a score tile
+constexpr int KC = BN / 16;     // 16-key chunks (K depth of P.V)
+constexpr int DB = D / 32;      // 32-wide output blocks
+constexpr int QS = D / 16;      // MFMAs per 32x32 score block
+static_assert(DMA == 2, "8 waves x 2 loads cover a 16 KB tile");
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unless exceeded by 2^8
+constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource (gfx9 family)
+
+// XOR swizzles of the 16-byte chunks of a K row (16 rows at one logical chunk
+// hit 16 distinct chunks) and of a V row (the 4 rows of a transposing read hit
+// disjoint 32-byte pairs), which keep the operand reads free of bank conflicts.
+__device__ __forceinline__ int k_swizzle(int row) { return row & 15; }
+__device__ __forceinline__ int v_swizzle(int row) { return (0xCA60 >> (4 * (row & 3))) & 15; }
+
+// This wave's share of one K or V tile, HBM -> LDS: DMA wave-wide loads, lane l
+// of load t filling the 16 bytes at dst + 1024 t + 16 l. The tile is read
+// through a raw buffer that starts at its first row and ends at the end of
+// the sequence, so rows at or past Sk fall outside it and load as zeros.
+__device__ __forceinline__ void dma_tile(const unsigned char* base, int kt, int seq_bytes, const unsigned* off,
+                                         unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * TILE), (short)0, seq_bytes - kt * TILE, kBufferConfig);
+#pragma unroll
+  for (int t = 0; t < DMA; ++t)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
+constexpr int kWaitLgkm0 = 0xC07F;       // lgkmcnt(0), others unconstrained
+constexpr int kWaitVm0Lgkm0 = 0x0070;    // vmcnt(0) lgkmcnt(0)
+
+// Workgroup barrier after the given s_waitcnt. No memory fence: a release
+// fence on LDS would also wait for every LDS DMA still in flight, which the
+// even phases must not do. The empty asm statements keep the compiler from
+// moving memory accesses across the barrier; the explicit wait makes this
+// wave's LDS reads (and, with vmcnt(0), its DMA into LDS) complete first.
+template <int WAIT>
+__device__ __forceinline__ void barrier_after() {
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_pp_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+  const int group = wave >> 2;                      // 0: M on even phases, 1: M on odd phases
+  const int row_block = 2 * (wave & 3) + group;     // the SIMD's two waves own adjacent blocks
+
+  // ---- work item: (q-tile, batch, query head) ------------------------------
+  int qt_seq, b, hq;
+  if (p.xcd_remap) {
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;
+    const int per_qt = (p.B * p.Hkv / 8) * p.group;
+    qt_seq = j / per_qt;
+    const int rem = j - qt_seq * per_qt;
+    const int pair = (rem / p.group) * 8 + xcd;
+    const int gq = rem - (rem / p.group) * p.group;
+    b = pair / p.Hkv;
+    hq = (pair - b * p.Hkv) * p.group + gq;
+  } else {
+    const int BH = p.B * p.Hq;
+    qt_seq = blockIdx.x / BH;
+    const int rem = blockIdx.x - qt_seq * BH;
+    b = rem / p.Hq;
+    hq = rem - b * p.Hq;
+  }
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_seq) : qt_seq;
+  const int hk = hq / p.group;
+
+  const int q0 = qt * BM;
+  const int qw = q0 + row_block * 32;
+  const int qi = qw + i32;
+
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * RB;
+  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * RB;
+  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * RB;
+  const int kv_bytes = p.Sk * RB;
+
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int n_tiles = (kv_end + BN - 1) / BN;  // tiles any wave of the workgroup needs
+  const bool wave_active = qw < p.Sq;
+  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
+  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1) / BN) : p.Sk / BN;
+
+  // ---- DMA: wave w writes 1 KB blocks DMA*w .. DMA*w+DMA-1 of each tile ----
+  unsigned kdma_off[DMA], vdma_off[DMA];
+  const int dma_pchunk = lane % CH;
+#pragma unroll
+  for (int t = 0; t < DMA; ++t) {
+    const int row = (64 * (DMA * wave + t) + lane) / CH;
+    kdma_off[t] = row * RB + 16 * (dma_pchunk ^ k_swizzle(row));
+    vdma_off[t] = row * RB + 16 * (dma_pchunk ^ v_swizzle(row));
+  }
+  const int dma_dst = 1024 * DMA * wave;
+
+  // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
+  u32x4 qf[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s)
+    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * RB + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+
+  int k_rd[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) k_rd[s] = i32 * RB + 16 * ((2 * s + g) ^ k_swizzle(i32));
+  const int J = lane & 15;
+  int v_rd[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int row = 4 * g + (J >> 2);
+    const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
+    v_rd[db] = row * RB + 16 * ((d >> 3) ^ v_swizzle(row)) + 2 * (d & 7);
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  f32x16 s[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+  u32x4 pf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) pf[kc] = u32x4{0, 0, 0, 0};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c = p.qk_scale_log2;
+  const bf16x2 ones = {(bf16_t)1.0f, (bf16_t)1.0f};
+
+  // M phase m with K(m) in kl and V(m-1) in vl.
+  auto pv_part = [&](const unsigned char* vl) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc) * RB + v_rd[db]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc + 8) * RB + v_rd[db]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
+      }
+  };
+  auto qk_part = [&](const unsigned char* kl) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < QS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 a = *(const u32x4*)(kl + kb * 32 * RB + k_rd[st]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+      }
+  };
+  // M phase m (0 <= m <= T), one straight-line shape for every m: for m = 0
+  // the P operand is still zero and the V slot was zeroed in the prologue,
+  // so the product adds nothing; for m = T the K slot holds a stale tile and
+  // the scores it yields are never read. Each MFMA is issued with the
+  // operand reads of the MFMA two places later.
+  auto m_phase = [&](int m, const unsigned char* kl, const unsigned char* vl) {
+    if (m > T) return;
+    pv_part(vl);
+    qk_part(kl);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < KC * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KB * QS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // V phase v: mask, maximum, lazy rescale, probabilities and row sums of S(v).
+  auto v_phase = [&](int v) {
+    if (v < 0 || v >= T) return;
+    if (v >= full_tiles) {
+      // Register r of block kb on half g holds key v*BN + 4g + (32kb + 8(r/4) + r%4);
+      // the key is visible iff that offset <= last visible key - v*BN - 4g.
+      const int limit = (CAUSAL ? min(p.Sk - 1, qi) : p.Sk - 1) - v * BN - 4 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) <= limit) ? s[kb][r] : -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float m_tile = halfwave_max(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 8 * j + 2 * e2;
+          const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_run));
+          const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_run));
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pf[2 * kb + j][e2] = w;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+        }
+  };
+
+  // DMA issued at the start of global phase 2n: K(n+1) and V(n).
+  auto dma_phase = [&](int n, unsigned char* k_dst, unsigned char* v_dst) {
+    if (n + 1 < n_tiles) dma_tile(kbase, n + 1, kv_bytes, kdma_off, k_dst + dma_dst);
+    if (n < n_tiles) dma_tile(vbase, n, kv_bytes, vdma_off, v_dst + dma_dst);
+  };
+
+  // ---- prologue: K(0) into slot 0 and V slot 1 zeroed (read by M(0)),
+  // published before phase 0 ----------------------------------------------------
+  if (n_tiles > 0) dma_tile(kbase, 0, kv_bytes, kdma_off, k_lds0 + dma_dst);
+#pragma unroll
+  for (int t = 0; t < TILE / (16 * 64 * WAVES); ++t)
+    *(u32x4*)(v_lds1 + 16 * (tid + 64 * WAVES * t)) = u32x4{0, 0, 0, 0};
+  barrier_after<kWaitVm0Lgkm0>();
+
+  // ---- global phases ----------------------------------------------------------
+  // Global phase p ends with a barrier that waits for this wave's LDS reads
+  // and, when p is odd, for the DMA issued at the start of phase p-1.
+  //   phase 4k   : DMA K(2k+1)->k1, V(2k)->v0 | A: M(2k)   [k0, v1] | B: V(2k-1)
+  //   phase 4k+1 :                            | A: V(2k)            | B: M(2k)   [k0, v1]
+  //   phase 4k+2 : DMA K(2k+2)->k0, V(2k+1)->v1 | A: M(2k+1) [k1, v0] | B: V(2k)
+  //   phase 4k+3 :                            | A: V(2k+1)          | B: M(2k+1) [k1, v0]
+  // Each group runs its own loop of four-phase trips, so a score tile never
+  // crosses a trip; both loops execute n_trips * 4 + 2 barriers.
+  const int n_trips = (n_tiles + 2) / 2;  // covers M(0..n_tiles) and V(0..n_tiles-1)
+  if (group == 0) {
+    for (int k = 0; k < n_trips; ++k) {
+      dma_phase(2 * k, k_lds1, v_lds0);
+      m_phase(2 * k, k_lds0, v_lds1);
+      barrier_after<kWaitLgkm0>();
+      v_phase(2 * k);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 1, k_lds0, v_lds1);
+      m_phase(2 * k + 1, k_lds1, v_lds0);
+      barrier_after<kWaitLgkm0>();
+      v_phase(2 * k + 1);
+      barrier_after<kWaitVm0Lgkm0>();
+    }
+    dma_phase(2 * n_trips, k_lds1, v_lds0);  // phase 4 n_trips: nothing left to compute
+    barrier_after<kWaitLgkm0>();
+  } else {
+    dma_phase(0, k_lds1, v_lds0);  // phase 0: no score tile yet
+    barrier_after<kWaitLgkm0>();
+    for (int k = 0; k < n_trips; ++k) {
+      m_phase(2 * k, k_lds0, v_lds1);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 1, k_lds0, v_lds1);
+      v_phase(2 * k);
+      barrier_after<kWaitLgkm0>();
+      m_phase(2 * k + 1, k_lds1, v_lds0);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 2, k_lds1, v_lds0);
+      v_phase(2 * k + 1);
+      barrier_after<kWaitLgkm0>();
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  if (!wave_active) return;
+  const float l_tot = halfwave_sum(l_run);
+  if (qi >= p.Sq) return;
+  const float inv = 1.0f / l_tot;
+  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)RB;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;
+      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+    }
+  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+}  // namespace pp
+
+int bf16_pp_block_m() { return pp::BM; }
+
+hipError_t launch_attn_bf16_pp(const AttnParams& p, bool causal, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  const void* fn = causal ? (const void*)&pp::attn_fwd_bf16_pp_kernel<true>
+                          : (const void*)&pp::attn_fwd_bf16_pp_kernel<false>;
+  return hipLaunchKernel(fn, dim3(grid), dim3(pp::WAVES * 64), args, 0, stream);
+}
+
+}  // namespace sdpa18

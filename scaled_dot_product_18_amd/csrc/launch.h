@@ -11,10 +11,14 @@ namespace sdpa18 {
 // ceil(Sq / block_m) x B x Hq workgroups).
 int mfma_block_m();
 int f32_block_m();
-int bf16_block_m();
+int bf16_block_m(int d);
+int bf16_pp_block_m();
 
 // bf16 inputs and output; d in {64, 128}.
 hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream);
+
+// bf16, d = 128: eight waves in matrix-core / vector-unit ping-pong.
+hipError_t launch_attn_bf16_pp(const AttnParams& p, bool causal, hipStream_t stream);
 
 // fp8-e4m3fn (fp8 = true) or bf16 inputs, bf16 output; d in {64, 128}.
 hipError_t launch_attn_mfma(const AttnParams& p, int d, bool causal, bool fp8, hipStream_t stream);

@@ -74,10 +74,11 @@ def test_cross_attention_lengths(gpu, dtype, Sq, Sk):
     _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, 128 if dtype != "f32" else 64, dtype, False, seed=Sq * 7 + Sk))
 
 
-def test_batch_and_heads_mapping(gpu):
+@pytest.mark.parametrize("d", [64, 128])
+def test_batch_and_heads_mapping(gpu, d):
     """Several batches and GQA groups at once, causal, lse on."""
     for dtype in ("f32", "bf16", "fp8"):
-        _run_full(sdpa_inputs.custom(3, 12, 3, 200, 200, 64, dtype, True, seed=55))
+        _run_full(sdpa_inputs.custom(3, 12, 3, 200, 200, d, dtype, True, seed=55))
 
 
 # ------------------------------------------------------------- golden fixtures
@@ -106,11 +107,12 @@ def test_golden_fixtures_fp32(gpu):
 
 # ----------------------------------------------------------------- properties
 
-def test_large_score_offset(gpu):
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_score_offset(gpu, d):
     """Scores around 1e3: the online softmax stays finite and matches the oracle."""
     import scaled_dot_product_18_amd as sdpa
     g = torch.Generator().manual_seed(5)
-    S, d = 150, 64
+    S = 150
     base = torch.full((1, 2, S, d), 4.0)
     q = (base + 0.1 * torch.randn(1, 2, S, d, generator=g)).to(torch.bfloat16)
     k = (base + 0.1 * torch.randn(1, 2, S, d, generator=g)).to(torch.bfloat16)
@@ -122,6 +124,30 @@ def test_large_score_offset(gpu):
         assert np.all(l_ref > 900)
         assert np.abs(o.double().cpu().numpy() - o_ref).max() <= TOL_O["bf16"]
         assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= 1e-5 * 1000 + 4e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference(gpu, d, causal):
+    """Scores that grow along the key sequence by ~100 (natural-log units) force the
+    running maximum to move many times mid-row; the result still matches the oracle."""
+    import scaled_dot_product_18_amd as sdpa
+    g = torch.Generator().manual_seed(77)
+    S = 700
+    q = torch.ones(1, 2, S, d) + 0.05 * torch.randn(1, 2, S, d, generator=g)
+    ramp = torch.linspace(0.0, 1.0, S).view(1, 1, S, 1)
+    k = 0.25 * torch.randn(1, 2, S, d, generator=g) + ramp * 100.0 / (d ** 0.5)
+    v = torch.randn(1, 2, S, d, generator=g)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    scale = 1.0 / d ** 0.5
+    o, lse = sdpa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, want_lse=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, causal)
+    qd, kd = q.double(), k.double()
+    rise = scale * ((qd[:, :, -1] * kd[:, :, -1]).sum(-1) - (qd[:, :, -1] * kd[:, :, 0]).sum(-1))
+    assert float(rise.min()) > 50  # the last query's scores climb by > 50 along its keys
+    assert np.abs(o.double().cpu().numpy() - o_ref).max() <= TOL_O["bf16"]
+    assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= 4e-3 + 1e-5 * np.abs(l_ref).max()
 
 
 def test_every_output_written(gpu):
@@ -149,17 +175,17 @@ def test_deterministic(gpu):
     assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l2) and torch.equal(l1, l3)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
-def test_gqa_equals_mha_on_repeated_kv(gpu, dtype):
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("fp8", 64), ("fp8", 128)])
+def test_gqa_equals_mha_on_repeated_kv(gpu, dtype, d):
     """GQA/MQA output is bit-identical to MHA on host-repeated K/V heads."""
     for Hkv in (2, 1):
-        w = sdpa_inputs.custom(2, 8, Hkv, 190, 190, 64, dtype, True, seed=21)
+        w = sdpa_inputs.custom(2, 8, Hkv, 190, 190, d, dtype, True, seed=21)
         inp = sdpa_inputs.make_inputs(w)
         o_g, l_g = run_gpu(w, to_device(inp))
         G = 8 // Hkv
         rep = dict(inp, k=inp["k"].repeat_interleave(G, dim=1).contiguous(),
                    v=inp["v"].repeat_interleave(G, dim=1).contiguous())
-        w_m = sdpa_inputs.custom(2, 8, 8, 190, 190, 64, dtype, True, seed=21)
+        w_m = sdpa_inputs.custom(2, 8, 8, 190, 190, d, dtype, True, seed=21)
         o_m, l_m = run_gpu(w_m, to_device(rep))
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_m) and torch.equal(l_g, l_m)
@@ -176,8 +202,9 @@ def test_causal_first_row_is_v0(gpu):
     assert torch.allclose(lse[:, :, 0].cpu().double(), s0, atol=1e-4)
 
 
-def test_lse_optional(gpu):
-    w = sdpa_inputs.custom(1, 4, 4, 100, 100, 64, "bf16", False, seed=41)
+@pytest.mark.parametrize("d", [64, 128])
+def test_lse_optional(gpu, d):
+    w = sdpa_inputs.custom(1, 4, 4, 100, 100, d, "bf16", False, seed=41)
     dev = to_device(sdpa_inputs.make_inputs(w))
     o1, lse = run_gpu(w, dev, want_lse=False)
     o2, _ = run_gpu(w, dev, want_lse=True)
