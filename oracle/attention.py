@@ -15,9 +15,14 @@ b, query head h and query row i,
   4. stats    lse[b,h,i] = max s + ln sum_j exp(s_j - max s)
 
 where
-  * allowed keys are all j in [0, Sk), or j <= i under the causal mask
-    (codelab section 7: the lower-triangular mask; the query sequence and key
-    sequence are the same sequence, so Sq == Sk is required);
+  * allowed keys are all j in [0, Sk), or j <= i + (Sk - Sq) under the causal
+    mask. With Sq == Sk this is the codelab's lower-triangular mask (section 7:
+    the first position sees only itself, the last sees every position). With
+    Sq < Sk the queries are the last Sq positions of the key sequence, as when
+    new tokens attend to a KV cache (codelab section 9): the last query still
+    sees every key (bottom-right alignment; the pages fix no rule for Sq != Sk,
+    this is the reading that keeps their first/last-position statement). Sq >
+    Sk under the mask would leave rows with no key and is rejected;
   * hk = h // (Hq // Hkv): consecutive query heads share one KV head
     (codelab section 9: fewer KV heads are broadcast over the query heads,
     e.g. 2 KV heads each serving 4 of 8 query heads);
@@ -47,18 +52,19 @@ def _check(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool) -> Tuple[i
         raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
     if Hkv < 1 or Hq % Hkv != 0:
         raise ValueError(f"Hq={Hq} is not a multiple of Hkv={Hkv}")
-    if causal and Sq != Sk:
-        raise ValueError("the causal mask is defined for self-attention (Sq == Sk)")
+    if causal and Sq > Sk:
+        raise ValueError("under the causal mask the first Sq - Sk query rows would see no key (Sq > Sk)")
     return B, Hq, Hkv, Sq, Sk, d
 
 
 def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   row_index: np.ndarray, causal: bool) -> Tuple[np.ndarray, np.ndarray]:
+                   row_index: np.ndarray, causal: bool, key_offset: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Attention for selected query rows of ONE (batch, head).
 
     q_rows [R, d] are the query vectors, row_index [R] their positions in the
-    query sequence (used only by the causal mask), k and v [Sk, d] that
-    head's keys and values. Returns (O [R, d], lse [R]) in fp64.
+    query sequence (used only by the causal mask, which lets row i see keys
+    j <= i + key_offset), k and v [Sk, d] that head's keys and values.
+    Returns (O [R, d], lse [R]) in fp64.
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -67,7 +73,7 @@ def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: floa
     s = (q_rows @ k.T) * float(scale)
     if causal:
         j = np.arange(k.shape[0])[None, :]
-        s = np.where(j <= np.asarray(row_index)[:, None], s, -np.inf)
+        s = np.where(j <= np.asarray(row_index)[:, None] + int(key_offset), s, -np.inf)
     # step 2: softmax over the allowed keys of each row
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -93,7 +99,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal:
             for i0 in range(0, Sq, row_block):
                 i1 = min(Sq, i0 + row_block)
                 o[b, h, i0:i1], lse[b, h, i0:i1] = attention_rows(
-                    q[b, h, i0:i1], k[b, hk], v[b, hk], scale, np.arange(i0, i1), causal)
+                    q[b, h, i0:i1], k[b, hk], v[b, hk], scale, np.arange(i0, i1), causal, Sk - Sq)
     return o, lse
 
 
@@ -111,7 +117,7 @@ def attention_sampled(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     out = []
     for b, h, rows in samples:
         rows = np.asarray(rows, dtype=np.int64)
-        o, lse = attention_rows(q[b, h, rows], k[b, h // G], v[b, h // G], scale, rows, causal)
+        o, lse = attention_rows(q[b, h, rows], k[b, h // G], v[b, h // G], scale, rows, causal, Sk - Sq)
         out.append((b, h, rows, o, lse))
     return out
 

@@ -146,7 +146,7 @@ def _decimal_attention(q, k, v, scale, causal):
         for h in range(Hq):
             hk = h // G
             for i in range(Sq):
-                js = [j for j in range(Sk) if (not causal) or j <= i]
+                js = [j for j in range(Sk) if (not causal) or j <= i + Sk - Sq]
                 s = [D(scale) * sum(D(q[b, h, i, c]) * D(k[b, hk, j, c]) for c in range(d)) for j in js]
                 e = [x.exp() for x in s]
                 den = sum(e)
@@ -157,11 +157,13 @@ def _decimal_attention(q, k, v, scale, causal):
 
 
 def pin_decimal_bruteforce(attn):
-    """50-digit Decimal evaluation of the definition on tiny inputs (S <= 4, d <= 4)."""
-    for (B, Hq, Hkv, S, d, causal, sc) in [(1, 1, 1, 4, 4, False, 0.5), (1, 2, 1, 4, 3, True, 0.9),
-                                           (2, 4, 2, 3, 2, False, 1.3), (1, 2, 2, 1, 4, True, 0.5),
-                                           (1, 1, 1, 4, 1, True, 2.0)]:
-        q, k, v = _rand(B, Hq, S, d, scale=1.5), _rand(B, Hkv, S, d, scale=1.5), _rand(B, Hkv, S, d)
+    """50-digit Decimal evaluation of the definition on tiny inputs (S <= 5, d <= 4), including
+    queries that are the last Sq of Sk positions."""
+    for (B, Hq, Hkv, Sq, Sk, d, causal, sc) in [(1, 1, 1, 4, 4, 4, False, 0.5), (1, 2, 1, 4, 4, 3, True, 0.9),
+                                                (2, 4, 2, 3, 3, 2, False, 1.3), (1, 2, 2, 1, 1, 4, True, 0.5),
+                                                (1, 1, 1, 4, 4, 1, True, 2.0), (1, 2, 1, 2, 5, 3, True, 0.8),
+                                                (1, 1, 1, 3, 5, 2, False, 1.1)]:
+        q, k, v = _rand(B, Hq, Sq, d, scale=1.5), _rand(B, Hkv, Sk, d, scale=1.5), _rand(B, Hkv, Sk, d)
         o, lse = attn(q, k, v, sc, causal)
         o_ref, lse_ref = _decimal_attention(q, k, v, sc, causal)
         np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-14)
@@ -184,9 +186,42 @@ def pin_torch_library(attn):
         np.testing.assert_allclose(lse, tlse.numpy(), atol=1e-12)
 
 
+def pin_queries_at_the_end(attn):
+    """Causal Sq < Sk: the queries are the last Sq positions. Their rows equal the last Sq rows of
+    the square causal problem whose earlier query rows are arbitrary; the last row sees every key,
+    so it equals the unmasked row; a single query (decode) is unmasked."""
+    B, Hq, Hkv, Sq, Sk, d, sc = 2, 4, 2, 5, 19, 8, 0.45
+    q, k, v = _rand(B, Hq, Sq, d), _rand(B, Hkv, Sk, d), _rand(B, Hkv, Sk, d)
+    o, lse = attn(q, k, v, sc, True)
+    q_full = np.concatenate([_rand(B, Hq, Sk - Sq, d), q], axis=2)
+    of, lf = attn(q_full, k, v, sc, True)
+    np.testing.assert_allclose(o, of[:, :, Sk - Sq:], atol=1e-13)
+    np.testing.assert_allclose(lse, lf[:, :, Sk - Sq:], atol=1e-13)
+    on, ln_ = attn(q, k, v, sc, False)
+    np.testing.assert_allclose(o[:, :, -1], on[:, :, -1], atol=1e-13)
+    assert np.max(np.abs(o[:, :, 0] - on[:, :, 0])) > 1e-3
+    o1, l1 = attn(q[:, :, -1:], k, v, sc, True)
+    np.testing.assert_allclose(o1, on[:, :, -1:], atol=1e-13)
+    np.testing.assert_allclose(l1, ln_[:, :, -1:], atol=1e-13)
+
+
+def pin_split_keys_merge(attn):
+    """Attention over two disjoint key sets combines through the row statistic: with
+    lse = ln(exp lse1 + exp lse2), O = exp(lse1 - lse) O1 + exp(lse2 - lse) O2."""
+    B, Hq, Hkv, Sq, Sk, d, sc = 1, 4, 1, 3, 23, 8, 0.6
+    q, k, v = _rand(B, Hq, Sq, d), _rand(B, Hkv, Sk, d, scale=2.0), _rand(B, Hkv, Sk, d)
+    o, lse = attn(q, k, v, sc, False)
+    c = 9
+    o1, l1 = attn(q, k[:, :, :c], v[:, :, :c], sc, False)
+    o2, l2 = attn(q, k[:, :, c:], v[:, :, c:], sc, False)
+    lm = np.logaddexp(l1, l2)
+    np.testing.assert_allclose(lm, lse, atol=1e-13)
+    np.testing.assert_allclose(np.exp(l1 - lm)[..., None] * o1 + np.exp(l2 - lm)[..., None] * o2, o, atol=1e-13)
+
+
 PINS = [pin_golden, pin_single_key, pin_rows_sum_to_one, pin_equal_keys_mean, pin_causal_first_last,
         pin_gqa_is_repeated_mha, pin_shift_affine_permutation, pin_large_offset, pin_decimal_bruteforce,
-        pin_torch_library]
+        pin_torch_library, pin_queries_at_the_end, pin_split_keys_merge]
 
 
 def _oracle(q, k, v, scale, causal):
@@ -212,7 +247,8 @@ def test_oracle_rejects_bad_shapes():
     with pytest.raises(ValueError):
         oracle.attention(q, k, k, 1.0)
     with pytest.raises(ValueError):
-        oracle.attention(np.zeros((1, 2, 3, 8)), k, k, 1.0, causal=True)
+        oracle.attention(np.zeros((1, 2, 5, 8)), k, k, 1.0, causal=True)
+    oracle.attention(np.zeros((1, 2, 3, 8)), k, k, 1.0, causal=True)
 
 
 # --------------------------------------------------------------------- E4M3 decoder
@@ -251,7 +287,8 @@ def _mutant(kind):
                 if causal:
                     i = np.arange(Sq)[:, None]
                     j = np.arange(Sk)[None, :]
-                    keep = (j <= i + 1) if kind == "causal_off_by_one" else (j <= i)
+                    off = 0 if kind == "top_left" else Sk - Sq
+                    keep = (j <= i + off + 1) if kind == "causal_off_by_one" else (j <= i + off)
                     s = np.where(keep, s, -np.inf)
                 if kind == "no_max":
                     e = np.exp(s)
@@ -268,7 +305,7 @@ def _mutant(kind):
 
 
 MUTANTS = ["no_scale", "neg_sign", "swap_kv", "head_modulo", "causal_off_by_one", "lse_log2", "no_max",
-           "transpose_w"]
+           "transpose_w", "top_left"]
 
 
 @pytest.mark.parametrize("kind", MUTANTS)
