@@ -47,15 +47,21 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 (16 hex digits) over every kernel and launch source: a counter
-    summary taken on other sources no longer describes the kernel."""
+# Source file of each kernel family; its counter summaries are keyed on it.
+KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
+                  "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip"}
+SHARED_SOURCES = ("kernel_common.h", "launch.h", "attn_api.cpp")
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 (16 hex digits) over a kernel's source file and the sources every
+    launch shares: a counter summary taken on other sources no longer
+    describes the kernel."""
     h = hashlib.sha256()
-    for fn in sorted(os.listdir(CSRC)):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(fn.encode())
-            with open(os.path.join(CSRC, fn), "rb") as f:
-                h.update(f.read())
+    for fn in (KERNEL_SOURCES[kernel],) + SHARED_SOURCES:
+        h.update(fn.encode())
+        with open(os.path.join(CSRC, fn), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -79,7 +85,7 @@ def traffic_from_profiles(w):
             key, sep, val = line.partition(":")
             if sep:
                 rec[key.strip()] = val.strip()
-    if rec.get("kernel_source_sha") != kernel_source_hash():
+    if rec.get("kernel_source_sha") != kernel_source_hash(kernel_name(w)):
         return None
     try:
         return float(rec["hbm_bytes_per_launch"])
@@ -252,7 +258,7 @@ def main() -> int:
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
         },
         "cpu_baseline": None,
-        "kernel_source_sha": kernel_source_hash(),
+        "kernel_source_sha": kernel_source_hash(kernel_name(w)),
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:

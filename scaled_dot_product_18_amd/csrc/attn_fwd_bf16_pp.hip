@@ -12,8 +12,8 @@
 //
 // Work of one wave (32 query rows) over its T key tiles of 64 keys is a chain
 // of phases  M0 V0 M1 V1 ... M(T-1) V(T-1) MT:
-//   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T   (32 MFMAs)
-//   V(m): mask, row max, lazy rescale, P(m) = exp2(S(m) c - m_ref), row sums
+//   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T - m_ref   (32 MFMAs)
+//   V(m): mask, P(m) = exp2(c S(m)), row sums, reference check
 // A workgroup holds 8 waves, two per SIMD: group A (waves 0-3) runs M phases
 // on even global phases and V phases on odd ones, group B (waves 4-7) the
 // other way round, so on every SIMD one wave feeds the matrix core while the
@@ -32,9 +32,16 @@
 // transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one query
 // column; the bf16-rounded score accumulator is directly the P^T operand; V^T
 // comes from the row-major V tile through ds_read_b64_tr_b16; XOR swizzles
-// keep the operand reads free of bank conflicts; the running maximum only
-// moves when a tile exceeds it by 2^8 (exact: softmax does not depend on the
-// reference point); row sums use v_dot2_f32_bf16 on the bf16 probabilities.
+// keep the operand reads free of bank conflicts.
+//
+// Softmax reference: the first Q.K^T MFMA of a tile starts from an accumulator
+// holding -m_ref, so the scores arrive relative to a reference maximum and the
+// vector unit only multiplies by c = scale*log2(e) and exponentiates. The
+// reference is set from the first tile's maximum and moves only when a tile's
+// partial row sums show probabilities above 2^12; softmax does not depend on
+// the reference point, so this is exact and the per-tile row maximum is gone.
+// Row sums are fp32 adds of the probabilities (v_dot2 on the packed values
+// would stall the partner wave's matrix core).
 #include "kernel_common.h"
 #include "launch.h"
 
@@ -44,7 +51,6 @@ namespace pp {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int WAVES = 8;
@@ -60,7 +66,10 @@ constexpr int DB = D / 32;      // 32-wide output blocks
 constexpr int QS = D / 16;      // MFMAs per 32x32 score block
 static_assert(DMA == 2, "8 waves x 2 loads cover a 16 KB tile");
 
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unless exceeded by 2^8
+constexpr int LA = 4;  // MFMAs whose LDS operand reads are in flight ahead of the matrix core
+// A lane's partial row sum of one tile above this (or not finite) makes the
+// wave move its reference maximum; below it every probability is <= 2^12.
+constexpr float kSumLimit = 4096.0f;
 constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource (gfx9 family)
 
 // XOR swizzles of the 16-byte chunks of a K row (16 rows at one logical chunk
@@ -166,6 +175,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const int dma_dst = 1024 * DMA * wave;
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
+  const float c = p.qk_scale_log2;
   u32x4 qf[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s)
@@ -192,10 +202,12 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   u32x4 pf[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) pf[kc] = u32x4{0, 0, 0, 0};
-  float m_run = -INFINITY;
+  // Reference maximum m_ref (dot-product units, equal on both halves of a
+  // query) and its negation replicated over an accumulator block: the first
+  // Q.K^T MFMA of a tile starts from it, so the scores arrive as s - m_ref.
+  float m_ref = 0.f;
+  f32x16 negm = f32x16{};
   float l_run = 0.f;
-  const float c = p.qk_scale_log2;
-  const bf16x2 ones = {(bf16_t)1.0f, (bf16_t)1.0f};
 
   // M phase m with K(m) in kl and V(m-1) in vl.
   auto pv_part = [&](const unsigned char* vl) {
@@ -211,39 +223,62 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   };
   auto qk_part = [&](const unsigned char* kl) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
     for (int st = 0; st < QS; ++st)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const u32x4 a = *(const u32x4*)(kl + kb * 32 * RB + k_rd[st]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+                                                        __builtin_bit_cast(bf16x8, qf[st]), st == 0 ? negm : s[kb],
+                                                        0, 0, 0);
       }
   };
   // M phase m (0 <= m <= T), one straight-line shape for every m: for m = 0
   // the P operand is still zero and the V slot was zeroed in the prologue,
   // so the product adds nothing; for m = T the K slot holds a stale tile and
-  // the scores it yields are never read. Each MFMA is issued with the
-  // operand reads of the MFMA two places later.
+  // the scores it yields are never read. The LDS operand reads run LA MFMAs
+  // ahead of the matrix core (two transposing reads per P.V MFMA, one read
+  // per Q.K^T MFMA).
   auto m_phase = [&](int m, const unsigned char* kl, const unsigned char* vl) {
     if (m > T) return;
     pv_part(vl);
     qk_part(kl);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    constexpr int NPV = KC * DB, NMF = KC * DB + KB * QS;
+    static_assert(LA <= NPV, "the prologue reads belong to P.V MFMAs");
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
 #pragma unroll
-    for (int i = 0; i < KC * DB; ++i) {
+    for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < KB * QS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      const int j = i + LA;
+      if (j < NPV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (j < NMF)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
 
-  // V phase v: mask, maximum, lazy rescale, probabilities and row sums of S(v).
+  // p = exp2(c S) for the whole tile: the P^T operand of the next M phase
+  // (rounded to bf16) and this lane's partial row sum (fp32, unrounded).
+  auto exp_tile = [&]() -> float {
+    float lt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 8 * j + 2 * e2;
+          const float p0 = exp2_fast(s[kb][r] * c), p1 = exp2_fast(s[kb][r + 1] * c);
+          pf[2 * kb + j][e2] = pack_bf16x2(p0, p1);
+          lt[e2] += p0;
+          lt[e2] += p1;
+        }
+    return (lt[0] + lt[1]) + (lt[2] + lt[3]);
+  };
+
+  // V phase v: mask, probabilities and row sums of S(v). The scores already
+  // have m_ref subtracted; the reference only moves on the first tile and when
+  // a tile's partial sums show probabilities beyond 2^12 (softmax does not
+  // depend on the reference point, so the result is unchanged).
   auto v_phase = [&](int v) {
     if (v < 0 || v >= T) return;
     if (v >= full_tiles) {
@@ -256,33 +291,37 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
         for (int r = 0; r < 16; ++r)
           s[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3) <= limit) ? s[kb][r] : -INFINITY;
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    const float m_tile = halfwave_max(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = exp2_fast(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    float l_tile = 0.f;
+    bool rebase = (v == 0);
+    if (!rebase) {
+      l_tile = exp_tile();
+      rebase = __builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)) != 0;
     }
+    if (rebase) {
+      // Tile 0 always holds a visible key of every row (key 0), so its maximum is finite.
+      float mx = s[0][0];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = halfwave_max(mx);
+      const float delta = (v == 0) ? mx : fmaxf(mx, 0.f);
+      if (v > 0) {
+        const float alpha = exp2_fast(-delta * c);
+        l_run *= alpha;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int r = 8 * j + 2 * e2;
-          const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_run));
-          const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_run));
-          const uint32_t w = pack_bf16x2(p0, p1);
-          pf[2 * kb + j][e2] = w;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
-        }
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      m_ref += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+      l_tile = exp_tile();
+    }
+    l_run += l_tile;
   };
 
   // DMA issued at the start of global phase 2n: K(n+1) and V(n).
@@ -355,7 +394,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
       *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
                                       pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
     }
-  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace pp
