@@ -49,6 +49,7 @@ def log(msg: str) -> None:
 
 # Source file of each kernel family; its counter summaries are keyed on it.
 KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
+                  "attn_fwd_fp8_pp_kernel": "attn_fwd_fp8_pp.hip",
                   "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip"}
 SHARED_SOURCES = ("kernel_common.h", "launch.h", "attn_api.cpp")
 
@@ -68,6 +69,8 @@ def kernel_source_hash(kernel: str) -> str:
 def kernel_name(w) -> str:
     if w.dtype == "bf16" and w.d == 128:
         return "attn_fwd_bf16_pp_kernel"
+    if w.dtype == "fp8" and w.d == 128:
+        return "attn_fwd_fp8_pp_kernel"
     return {"f32": "attn_fwd_f32_kernel", "bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_mfma_kernel"}[w.dtype]
 
 

@@ -80,8 +80,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
         make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::bf16_block_m(d));
     return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
   }
-  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::mfma_block_m());
-  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, true, stream));
+  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::fp8_block_m(d));
+  return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int B, int Hq, int Hkv,
@@ -95,8 +95,8 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, f
   const float qk = scale * descale_q * descale_k;
   if (!positive_finite(qk * kLog2e)) return ATTN_ERR_SCALE;
   const sdpa18::AttnParams p =
-      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, qk, descale_v, sdpa18::mfma_block_m());
-  return launch_status(sdpa18::launch_attn_mfma(p, d, causal != 0, true, stream));
+      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, qk, descale_v, sdpa18::fp8_block_m(d));
+  return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
 const char* attn_strerror(int status) {

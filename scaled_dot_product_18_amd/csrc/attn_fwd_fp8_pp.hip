@@ -1,0 +1,413 @@
+// Fused scaled dot-product attention forward for gfx950 on fp8-e4m3fn inputs,
+// head dim 128: eight waves per workgroup in matrix-core / vector-unit
+// ping-pong, Q.K^T on fp8 matrix cores, P.V on bf16 matrix cores.
+//
+// The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
+// and FlashAttention", section 3): K and V stream through on-chip tiles, the
+// scores of a tile exist only in registers, a reference maximum and a
+// normaliser rescale the partial output as tiles arrive (online softmax), and
+// only O and the per-row log-sum-exp are written. The arithmetic is the
+// codelab's three steps ("Accelerate attention on GPU with cuDNN and
+// TransformerEngine", intro and section 4) with the lower-triangular mask of
+// its section 7, the shared KV heads of its section 9 and the E4M3 inputs
+// with per-tensor scales of its section 10.
+//
+// Structure (shared with the bf16 ping-pong kernel): each wave owns 32 query
+// rows and runs phases M0 V0 M1 V1 ... over its 64-key tiles; the two waves
+// of a SIMD are one phase apart, so one feeds the matrix core while the other
+// runs the softmax; a workgroup barrier separates phases.
+//   M(m): O^T += V(m-1)^T . P(m-1)^T  (16 bf16 MFMAs 32x32x16)
+//         S(m)^T = K(m) . Q^T - m_ref  (4 fp8 MFMAs 32x32x64, unit block scales)
+//   V(m): mask, P(m) = exp2(c S(m)), fp32 row sums, reference check
+// c = scale * descale_q * descale_k * log2(e); descale_v is applied to O.
+//
+// Memory path:
+//  * K tiles (fp8, 64 x 128 B = 8 KB) go HBM -> LDS by buffer_load ... lds;
+//    K rows are read in a bit-permuted order (bits 2 and 3 of the row swapped)
+//    so that each lane's 8 consecutive score registers hold 8 consecutive keys.
+//  * V tiles are loaded into registers, widened e4m3 -> bf16 (exact), and
+//    written to LDS transposed (V^T, keys contiguous per dimension), once per
+//    workgroup; every P.V operand is then one 16-byte LDS read.
+//  * Both LDS layouts carry an XOR swizzle of their 16-byte chunks that keeps
+//    the operand reads free of bank conflicts.
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace sdpa18 {
+namespace fp8pp {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int D = 128;
+constexpr int WAVES = 8;
+constexpr int BM = 32 * WAVES;       // query rows per workgroup
+constexpr int BN = 64;               // keys per tile
+constexpr int KRB = D;               // bytes per fp8 K row
+constexpr int KTILE = BN * KRB;      // 8 KB
+constexpr int VTRB = BN * 2;         // bytes per bf16 V^T row (64 keys)
+constexpr int VTILE = D * VTRB;      // 16 KB
+constexpr int KB = BN / 32;          // 32-key blocks of a score tile
+constexpr int KC = BN / 16;          // 16-key chunks (K depth of P.V)
+constexpr int DB = D / 32;           // 32-wide output blocks
+constexpr int QS = D / 64;           // fp8 MFMA steps of a 32x32 score block
+static_assert(KTILE == 1024 * WAVES, "one 1 KB K load per wave per tile");
+static_assert(BN * D == 16 * 64 * WAVES, "each lane stages 4 keys x 4 dims of V per tile");
+
+constexpr int LA = 4;                       // MFMAs whose LDS operand reads are in flight ahead
+constexpr float kSumLimit = 4096.0f;        // see the bf16 ping-pong kernel
+constexpr int kBufferConfig = 0x00020000;   // word 3 of a raw buffer resource (gfx9 family)
+constexpr int kE8M0One = 127;               // E8M0 block scale 2^0
+constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
+constexpr int kWaitVm0Lgkm0 = 0x0070;       // s_waitcnt vmcnt(0) lgkmcnt(0)
+
+// Chunk swizzle of both layouts: the 16 lanes of one read phase hit 8 even and
+// 8 odd rows at one logical chunk; XOR with (row >> 1) & 7 spreads each set
+// over all 8 chunk positions.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int WAIT>
+__device__ __forceinline__ void barrier_after() {
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_pp_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[VTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[VTILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+  const int group = wave >> 2;                   // 0: M on even phases, 1: M on odd phases
+  const int row_block = 2 * (wave & 3) + group;  // the SIMD's two waves own adjacent blocks
+
+  // ---- work item: (q-tile, batch, query head) ------------------------------
+  int qt_seq, b, hq;
+  if (p.xcd_remap) {
+    const int xcd = blockIdx.x & 7;
+    const int j = blockIdx.x >> 3;
+    const int per_qt = (p.B * p.Hkv / 8) * p.group;
+    qt_seq = j / per_qt;
+    const int rem = j - qt_seq * per_qt;
+    const int pair = (rem / p.group) * 8 + xcd;
+    const int gq = rem - (rem / p.group) * p.group;
+    b = pair / p.Hkv;
+    hq = (pair - b * p.Hkv) * p.group + gq;
+  } else {
+    const int BH = p.B * p.Hq;
+    qt_seq = blockIdx.x / BH;
+    const int rem = blockIdx.x - qt_seq * BH;
+    b = rem / p.Hq;
+    hq = rem - b * p.Hq;
+  }
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_seq) : qt_seq;
+  const int hk = hq / p.group;
+
+  const int q0 = qt * BM;
+  const int qw = q0 + row_block * 32;
+  const int qi = qw + i32;
+
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * KRB;
+  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * KRB;
+  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * KRB;
+  const int kv_bytes = p.Sk * KRB;
+
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const bool wave_active = qw < p.Sq;
+  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
+  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1) / BN) : p.Sk / BN;
+
+  // ---- K DMA: wave w fills rows 8w .. 8w+7 of a K tile (lane l: row 8w + l/8,
+  // physical chunk l%8) ------------------------------------------------------
+  const int kdma_row = 8 * wave + (lane >> 3);
+  const unsigned kdma_off = kdma_row * KRB + 16 * ((lane & 7) ^ swz(kdma_row));
+  const int kdma_dst = 1024 * wave;
+  auto dma_k = [&](int kt, unsigned char* dst) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + kt * KTILE), (short)0, kv_bytes - kt * KTILE, kBufferConfig);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kdma_dst), 16, kdma_off, 0, 0, 0);
+  };
+
+  // ---- V staging: lane l of wave w holds keys 4(l/4) .. +3 at dims 16w + 4(l%4) .. +3
+  const int vkg = lane >> 2;
+  const int vd0 = 16 * wave + 4 * (lane & 3);
+  uint32_t vreg[4];
+  auto load_v = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + kt * KTILE), (short)0, kv_bytes - kt * KTILE, kBufferConfig);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vreg[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (4 * vkg + j) * KRB + vd0, 0, 0);
+  };
+  // e4m3 -> bf16 (exact) and the transposed store: dimension vd0 + e gets the
+  // 4 keys' values as one 8-byte unit at key offset 4 vkg of its V^T row.
+  auto store_v = [&](unsigned char* dst) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vreg[j], 1.0f, false));
+      hi[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vreg[j], 1.0f, true));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t* w = (e < 2) ? lo : hi;
+      const u32x2 val = (e & 1) ? u32x2{pack_hi16(w[0], w[1]), pack_hi16(w[2], w[3])}
+                                : u32x2{pack_lo16(w[0], w[1]), pack_lo16(w[2], w[3])};
+      const int dd = vd0 + e;
+      *(u32x2*)(dst + dd * VTRB + 16 * ((vkg >> 1) ^ swz(dd)) + 8 * (vkg & 1)) = val;
+    }
+  };
+
+  // ---- Q fragment (B operand of S^T): step s, half g holds dims [64s+32g, +32)
+  const float c = p.qk_scale_log2;
+  i32x8 qf[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    u32x4 q0v = u32x4{0, 0, 0, 0}, q1v = u32x4{0, 0, 0, 0};
+    if (qi < p.Sq) {
+      q0v = *(const u32x4*)(qbase + (size_t)qi * KRB + 64 * s + 32 * g);
+      q1v = *(const u32x4*)(qbase + (size_t)qi * KRB + 64 * s + 32 * g + 16);
+    }
+    qf[s] = i32x8{(int)q0v[0], (int)q0v[1], (int)q0v[2], (int)q0v[3],
+                  (int)q1v[0], (int)q1v[1], (int)q1v[2], (int)q1v[3]};
+  }
+
+  // ---- LDS operand offsets ---------------------------------------------------
+  // K (A operand): row 32kb + swap_bits23(i32), logical chunks 4s + 2g and +1.
+  const int krow = swap_bits23(i32);
+  int k_rd[QS][2];
+#pragma unroll
+  for (int s = 0; s < QS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) k_rd[s][h] = krow * KRB + 16 * ((4 * s + 2 * g + h) ^ swz(krow));
+  // V^T (A operand): row 32db + i32, logical chunk 2kc + g (keys 16kc + 8g .. +7).
+  int v_rd[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) v_rd[kc] = i32 * VTRB + 16 * ((2 * kc + g) ^ swz(i32));
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  f32x16 s[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+  u32x4 pf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) pf[kc] = u32x4{0, 0, 0, 0};
+  // Reference maximum m_ref (dot-product units of the fp8 codes, equal on
+  // both halves of a query) and its negation replicated over an accumulator
+  // block: the first Q.K^T MFMA of a tile starts from it.
+  float m_ref = 0.f;
+  f32x16 negm = f32x16{};
+  float l_run = 0.f;
+
+  auto pv_part = [&](const unsigned char* vl) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 a = *(const u32x4*)(vl + db * 32 * VTRB + v_rd[kc]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
+      }
+  };
+  auto qk_part = [&](const unsigned char* kl) {
+#pragma unroll
+    for (int st = 0; st < QS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 a0 = *(const u32x4*)(kl + kb * 32 * KRB + k_rd[st][0]);
+        const u32x4 a1 = *(const u32x4*)(kl + kb * 32 * KRB + k_rd[st][1]);
+        const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[st], st == 0 ? negm : s[kb], 0, 0, 0,
+                                                                kE8M0One, 0, kE8M0One);
+      }
+  };
+  // M phase m (0 <= m <= T), one straight-line shape for every m (for m = 0 the
+  // P operand is zero and the V slot was zeroed; for m = T the scores are never
+  // read). LDS operand reads run LA MFMAs ahead.
+  auto m_phase = [&](int m, const unsigned char* kl, const unsigned char* vl) {
+    if (m > T) return;
+    pv_part(vl);
+    qk_part(kl);
+    constexpr int NPV = KC * DB, NMF = KC * DB + KB * QS;
+    static_assert(LA <= NPV, "the prologue reads belong to P.V MFMAs");
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int j = i + LA;
+      if (j < NPV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else if (j < NMF)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
+  // p = exp2(c S) for the whole tile: the P^T operand (bf16) and this lane's
+  // partial row sum (fp32, unrounded). Registers 8j .. 8j+7 of block kb hold
+  // keys 32kb + 16j + 8g .. +7, i.e. P^T chunk kc = 2kb + j.
+  auto exp_tile = [&]() -> float {
+    float lt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 8 * j + 2 * e2;
+          const float p0 = exp2_fast(s[kb][r] * c), p1 = exp2_fast(s[kb][r + 1] * c);
+          pf[2 * kb + j][e2] = pack_bf16x2(p0, p1);
+          lt[e2] += p0;
+          lt[e2] += p1;
+        }
+    return (lt[0] + lt[1]) + (lt[2] + lt[3]);
+  };
+
+  // V phase v: mask, probabilities and row sums of S(v); the reference moves
+  // on tile 0 and when a tile's partial sums show probabilities beyond 2^12.
+  auto v_phase = [&](int v) {
+    if (v < 0 || v >= T) return;
+    if (v >= full_tiles) {
+      // Register r of block kb on half g holds key v*BN + 32kb + 16(r/8) + 8g + r%8.
+      const int limit = (CAUSAL ? min(p.Sk - 1, qi) : p.Sk - 1) - v * BN - 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= limit) ? s[kb][r] : -INFINITY;
+    }
+    float l_tile = 0.f;
+    bool rebase = (v == 0);
+    if (!rebase) {
+      l_tile = exp_tile();
+      rebase = __builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)) != 0;
+    }
+    if (rebase) {
+      // Tile 0 holds key 0, visible to every row, so its maximum is finite.
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = halfwave_max(mx);
+      const float delta = (v == 0) ? mx : fmaxf(mx, 0.f);
+      if (v > 0) {
+        const float alpha = exp2_fast(-delta * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      m_ref += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+      l_tile = exp_tile();
+    }
+    l_run += l_tile;
+  };
+
+  // Loads issued at the start of global phase 2n: K(n+1) (DMA) and V(n) (to
+  // registers); V(n) is widened and stored at the end of phase 2n+1.
+  auto dma_phase = [&](int n, unsigned char* k_dst) {
+    if (n + 1 < n_tiles) dma_k(n + 1, k_dst);
+    if (n < n_tiles) load_v(n);
+  };
+  auto v_store_phase = [&](int n, unsigned char* v_dst) {
+    if (n < n_tiles) store_v(v_dst);
+  };
+
+  // ---- prologue: K(0) into slot 0, V^T slot 1 zeroed (read by M(0)) --------
+  if (n_tiles > 0) dma_k(0, k_lds0);
+#pragma unroll
+  for (int t = 0; t < VTILE / (16 * 64 * WAVES); ++t)
+    *(u32x4*)(v_lds1 + 16 * (tid + 64 * WAVES * t)) = u32x4{0, 0, 0, 0};
+  barrier_after<kWaitVm0Lgkm0>();
+
+  // ---- global phases (as the bf16 ping-pong kernel) -------------------------
+  //   phase 4k   : loads K(2k+1)->k1, V(2k)      | A: M(2k)   [k0, v1] | B: V(2k-1)
+  //   phase 4k+1 : store V(2k)->v0 at the end    | A: V(2k)            | B: M(2k)   [k0, v1]
+  //   phase 4k+2 : loads K(2k+2)->k0, V(2k+1)    | A: M(2k+1) [k1, v0] | B: V(2k)
+  //   phase 4k+3 : store V(2k+1)->v1 at the end  | A: V(2k+1)          | B: M(2k+1) [k1, v0]
+  const int n_trips = (n_tiles + 2) / 2;
+  if (group == 0) {
+    for (int k = 0; k < n_trips; ++k) {
+      dma_phase(2 * k, k_lds1);
+      m_phase(2 * k, k_lds0, v_lds1);
+      barrier_after<kWaitLgkm0>();
+      v_phase(2 * k);
+      v_store_phase(2 * k, v_lds0);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 1, k_lds0);
+      m_phase(2 * k + 1, k_lds1, v_lds0);
+      barrier_after<kWaitLgkm0>();
+      v_phase(2 * k + 1);
+      v_store_phase(2 * k + 1, v_lds1);
+      barrier_after<kWaitVm0Lgkm0>();
+    }
+    dma_phase(2 * n_trips, k_lds1);  // nothing left to load or compute
+    barrier_after<kWaitLgkm0>();
+  } else {
+    dma_phase(0, k_lds1);
+    barrier_after<kWaitLgkm0>();
+    for (int k = 0; k < n_trips; ++k) {
+      m_phase(2 * k, k_lds0, v_lds1);
+      v_store_phase(2 * k, v_lds0);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 1, k_lds0);
+      v_phase(2 * k);
+      barrier_after<kWaitLgkm0>();
+      m_phase(2 * k + 1, k_lds1, v_lds0);
+      v_store_phase(2 * k + 1, v_lds1);
+      barrier_after<kWaitVm0Lgkm0>();
+      dma_phase(2 * k + 2, k_lds1);
+      v_phase(2 * k + 1);
+      barrier_after<kWaitLgkm0>();
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  if (!wave_active) return;
+  const float l_tot = halfwave_sum(l_run);
+  if (qi >= p.Sq) return;
+  const float inv = p.o_scale / l_tot;
+  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)(D * 2);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;
+      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+    }
+  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
+}
+
+}  // namespace fp8pp
+
+int fp8_pp_block_m() { return fp8pp::BM; }
+
+hipError_t launch_attn_fp8_pp(const AttnParams& p, bool causal, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  AttnParams arg = p;
+  void* args[] = {&arg};
+  const void* fn = causal ? (const void*)&fp8pp::attn_fwd_fp8_pp_kernel<true>
+                          : (const void*)&fp8pp::attn_fwd_fp8_pp_kernel<false>;
+  return hipLaunchKernel(fn, dim3(grid), dim3(fp8pp::WAVES * 64), args, 0, stream);
+}
+
+}  // namespace sdpa18

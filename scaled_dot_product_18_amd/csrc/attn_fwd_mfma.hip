@@ -1,6 +1,8 @@
-// Fused scaled dot-product attention forward for gfx950 on 16-bit and 8-bit
-// matrix cores: bf16 inputs (bf16 MFMA for both products) and fp8-e4m3fn
-// inputs (fp8 MFMA for Q.K^T, bf16 MFMA for P.V with V widened exactly).
+// Fused scaled dot-product attention forward for gfx950 on fp8-e4m3fn inputs
+// at head dimension 64 (fp8 MFMA for Q.K^T, bf16 MFMA for P.V with V widened
+// exactly); head dimension 128 runs the ping-pong kernel of attn_fwd_fp8_pp.hip.
+// The template also has a bf16-input form (FP8 = false), which nothing
+// launches.
 //
 // The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
 // and FlashAttention", section 3): Q, K, V are cut into tiles that fit on chip,
@@ -315,15 +317,11 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   return hipLaunchKernel((const void*)&attn_fwd_mfma_kernel<D, CAUSAL, FP8>, dim3(grid), dim3(256), args, 0, stream);
 }
 
-int mfma_block_m() { return 128; }
+int fp8_block_m(int d) { return d == 128 ? fp8_pp_block_m() : 128; }
 
-hipError_t launch_attn_mfma(const AttnParams& p, int d, bool causal, bool fp8, hipStream_t stream) {
-  if (d == 128) {
-    if (fp8) return causal ? launch_one<128, true, true>(p, stream) : launch_one<128, false, true>(p, stream);
-    return causal ? launch_one<128, true, false>(p, stream) : launch_one<128, false, false>(p, stream);
-  }
-  if (fp8) return causal ? launch_one<64, true, true>(p, stream) : launch_one<64, false, true>(p, stream);
-  return causal ? launch_one<64, true, false>(p, stream) : launch_one<64, false, false>(p, stream);
+hipError_t launch_attn_fp8(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return launch_attn_fp8_pp(p, causal, stream);
+  return causal ? launch_one<64, true, true>(p, stream) : launch_one<64, false, true>(p, stream);
 }
 
 }  // namespace sdpa18
