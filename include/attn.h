@@ -9,8 +9,10 @@
  *   O[b,h,i,:] = sum_j softmax_j( scale * Q[b,h,i,:] . K[b,hk,j,:] ) * V[b,hk,j,:]
  *   lse[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,hk,j,:] )
  *
- * over the allowed keys j: all of [0, Sk), or j <= i with the causal
- * (lower-triangular) mask of the codelab's section 7. Query head h reads KV
+ * over the allowed keys j: all of [0, Sk), or j <= i + (Sk - Sq) with the
+ * causal (lower-triangular) mask of the codelab's section 7, the queries
+ * being the last Sq of the Sk positions (Sq == Sk is self-attention; Sq < Sk
+ * is new queries against a longer key sequence, as with a KV cache). Query head h reads KV
  * head hk = h / (Hq / Hkv): consecutive groups of query heads share one KV
  * head (MHA when Hkv == Hq, GQA, MQA when Hkv == 1; codelab section 9).
  * The computation is fused in the FlashAttention manner (article section 3):
@@ -59,7 +61,7 @@ enum {
   ATTN_ERR_SHAPE = -2,         /* a size is < 1, or the problem exceeds 32-bit indexing */
   ATTN_ERR_HEADS = -3,         /* Hq is not a multiple of Hkv                           */
   ATTN_ERR_HEADDIM = -4,       /* d is not 64 or 128                                    */
-  ATTN_ERR_CAUSAL_SHAPE = -5,  /* causal requested with Sq != Sk                        */
+  ATTN_ERR_CAUSAL_SHAPE = -5,  /* causal requested with Sq > Sk                         */
   ATTN_ERR_DTYPE = -6,         /* dtype is not an attn_dtype_t value                    */
   ATTN_ERR_SCALE = -7,         /* scale or a descale is not finite and > 0              */
   ATTN_ERR_ALIGN = -8,         /* a base pointer is not 16-byte aligned                 */
@@ -73,10 +75,11 @@ enum {
  *   o        device output: float32 for ATTN_F32, bfloat16 otherwise.
  *   lse      device float32 [B, Hq, Sq] or NULL to skip the statistic.
  *   B, Hq, Hkv, Sq, Sk, d   sizes; Hq % Hkv == 0; d in {64, 128};
- *            causal requires Sq == Sk (self-attention, codelab section 7).
+ *            causal requires Sq <= Sk.
  *   scale    multiplier of the dot products, finite and > 0 (the pages use
  *            1/sqrt(d)).
- *   causal   0 = every key visible; nonzero = key j visible to query i iff j <= i.
+ *   causal   0 = every key visible; nonzero = key j visible to query i iff
+ *            j <= i + (Sk - Sq).
  *   dtype    attn_dtype_t; ATTN_FP8_E4M3 here means all descales are 1.
  *   stream   HIP stream to enqueue on.
  *

@@ -31,13 +31,13 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  if (causal && Sq != Sk) return ATTN_ERR_CAUSAL_SHAPE;
+  if (causal && Sq > Sk) return ATTN_ERR_CAUSAL_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
   return ATTN_OK;
 }
 
 sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                               int Hkv, int Sq, int Sk, float qk_scale, float o_scale, int block_m) {
+                               int Hkv, int Sq, int Sk, int causal, float qk_scale, float o_scale, int block_m) {
   sdpa18::AttnParams p;
   p.q = q;
   p.k = k;
@@ -55,6 +55,8 @@ sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void
   p.o_scale = o_scale;
   // Each XCD gets whole KV heads when they split evenly over the 8 XCDs.
   p.xcd_remap = ((B * Hkv) % 8 == 0) ? 1 : 0;
+  // The queries are the last Sq of Sk positions: query i sits at position i + Sk - Sq.
+  p.causal_off = causal ? Sk - Sq : 0;
   return p;
 }
 
@@ -72,15 +74,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
   if (dtype == ATTN_F32) {
     const sdpa18::AttnParams p =
-        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::f32_block_m());
+        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::f32_block_m());
     return launch_status(sdpa18::launch_attn_f32(p, d, causal != 0, stream));
   }
   if (dtype == ATTN_BF16) {
     const sdpa18::AttnParams p =
-        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::bf16_block_m(d));
+        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::bf16_block_m(d));
     return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
   }
-  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, scale, 1.0f, sdpa18::fp8_block_m(d));
+  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::fp8_block_m(d));
   return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
@@ -95,7 +97,7 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, f
   const float qk = scale * descale_q * descale_k;
   if (!positive_finite(qk * kLog2e)) return ATTN_ERR_SCALE;
   const sdpa18::AttnParams p =
-      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, qk, descale_v, sdpa18::fp8_block_m(d));
+      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, causal, qk, descale_v, sdpa18::fp8_block_m(d));
   return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
@@ -106,7 +108,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_SHAPE: return "a size is < 1 or the problem exceeds 32-bit indexing";
     case ATTN_ERR_HEADS: return "Hq is not a multiple of Hkv";
     case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
-    case ATTN_ERR_CAUSAL_SHAPE: return "causal masking requires Sq == Sk";
+    case ATTN_ERR_CAUSAL_SHAPE: return "causal masking requires Sq <= Sk";
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_ALIGN: return "a base pointer is not 16-byte aligned";

@@ -142,10 +142,10 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::RB;
   const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * C::RB;
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
   const bool wave_active = qw < p.Sq;
-  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / C::BN + 1) : n_tiles);
+  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BN + 1) : n_tiles);
 
   // ---- DMA assignment: wave w writes 1 KB blocks 4w..4w+3 of each tile -----
   // 16-byte slot s = 64*(4w+t) + lane holds row s / CH, physical chunk s % CH.
@@ -208,13 +208,13 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
     }
 
     // register r of block kb on half g holds key kv0 + 32kb + 8(r/4) + 4g + r%4
-    if ((CAUSAL && kv0 + C::BN - 1 > qw) || kv0 + C::BN > p.Sk) {
+    if ((CAUSAL && kv0 + C::BN - 1 > qw + p.causal_off) || kv0 + C::BN > p.Sk) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi);
+          const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi + p.causal_off);
           s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
     }

@@ -157,11 +157,11 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * RB;
   const int kv_bytes = p.Sk * RB;
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;  // tiles any wave of the workgroup needs
   const bool wave_active = qw < p.Sq;
-  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
-  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1) / BN) : p.Sk / BN;
+  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / BN + 1) : n_tiles);
+  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1 + p.causal_off) / BN) : p.Sk / BN;
 
   // ---- DMA: wave w writes 1 KB blocks DMA*w .. DMA*w+DMA-1 of each tile ----
   unsigned kdma_off[DMA], vdma_off[DMA];
@@ -284,7 +284,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
     if (v >= full_tiles) {
       // Register r of block kb on half g holds key v*BN + 4g + (32kb + 8(r/4) + r%4);
       // the key is visible iff that offset <= last visible key - v*BN - 4g.
-      const int limit = (CAUSAL ? min(p.Sk - 1, qi) : p.Sk - 1) - v * BN - 4 * g;
+      const int limit = (CAUSAL ? min(p.Sk - 1, qi + p.causal_off) : p.Sk - 1) - v * BN - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

@@ -50,10 +50,10 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   const float* kbase = (const float*)p.k + kv_row0 * D;
   const float* vbase = (const float*)p.v + kv_row0 * D;
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const bool wave_active = qw < p.Sq;
-  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
+  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / BN + 1) : n_tiles);
 
   // Q fragment (B operand of S^T): step s, half g holds dim 2s + g.
   float qf[D / 2];
@@ -98,12 +98,12 @@ void attn_fwd_f32_kernel(const AttnParams p) {
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[i32 * KLD + 2 * st + g], qf[st], s, 0, 0, 0);
 
     // register r on half g holds key kv0 + 8(r/4) + 4g + (r%4)
-    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw) || (kv0 + BN > p.Sk);
+    const bool need_mask = (CAUSAL && kv0 + BN - 1 > qw + p.causal_off) || (kv0 + BN > p.Sk);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi);
+        const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi + p.causal_off);
         s[r] = ok ? s[r] : -INFINITY;
       }
     }

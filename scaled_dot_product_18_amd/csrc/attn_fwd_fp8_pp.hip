@@ -122,11 +122,11 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * KRB;
   const int kv_bytes = p.Sk * KRB;
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;
   const bool wave_active = qw < p.Sq;
-  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles);
-  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1) / BN) : p.Sk / BN;
+  const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / BN + 1) : n_tiles);
+  const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1 + p.causal_off) / BN) : p.Sk / BN;
 
   // ---- K DMA: wave w fills rows 8w .. 8w+7 of a K tile (lane l: row 8w + l/8,
   // physical chunk l%8) ------------------------------------------------------
@@ -281,7 +281,7 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
     if (v < 0 || v >= T) return;
     if (v >= full_tiles) {
       // Register r of block kb on half g holds key v*BN + 32kb + 16(r/8) + 8g + r%8.
-      const int limit = (CAUSAL ? min(p.Sk - 1, qi) : p.Sk - 1) - v * BN - 8 * g;
+      const int limit = (CAUSAL ? min(p.Sk - 1, qi + p.causal_off) : p.Sk - 1) - v * BN - 8 * g;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

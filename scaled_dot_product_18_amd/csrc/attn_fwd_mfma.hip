@@ -90,10 +90,10 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::KRB;
   const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * (size_t)(D * C::ES);
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
   const bool wave_active = qw < p.Sq;
-  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31) / C::BN + 1) : n_tiles);
+  const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BN + 1) : n_tiles);
 
   // ---- Q fragment: B operand of S^T = K.Q^T, resident for the whole loop ---
   // bf16: step s, lane half g holds dims [16s + 8g, +8); fp8: dims [64s + 32g, +32).
@@ -228,14 +228,14 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 
       // Mask keys beyond Sk and, when causal, keys after the query.
       // Accumulator register r of block kb on half g holds key 32kb + 16(r>>3) + 8g + (r&7).
-      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw) || (kv0 + C::BN > p.Sk);
+      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > qw + p.causal_off) || (kv0 + C::BN > p.Sk);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * g + (r & 7);
-            const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi);
+            const bool ok = (key < p.Sk) && (!CAUSAL || key <= qi + p.causal_off);
             s[kb][r] = ok ? s[kb][r] : -INFINITY;
           }
       }

@@ -30,6 +30,7 @@ struct AttnParams {
   float qk_scale_log2;  // scale * descale_q * descale_k * log2(e): scores enter exp2 directly
   float o_scale;        // descale_v (1 unless fp8 inputs)
   int xcd_remap;        // 1: order workgroups so each XCD owns whole KV heads ((B*Hkv) % 8 == 0)
+  int causal_off;       // Sk - Sq: under the causal mask query i sees keys j <= i + causal_off
 };
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

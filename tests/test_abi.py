@@ -72,7 +72,7 @@ def _call(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=64,
     (dict(Sq=1 << 30), -2),
     (dict(Hq=3, Hkv=2), -3),
     (dict(d=96), -4), (dict(d=256), -4), (dict(d=32), -4),
-    (dict(causal=1, Sq=8, Sk=9), -5),
+    (dict(causal=1, Sq=9, Sk=8), -5),
     (dict(dtype=3), -6), (dict(dtype=-1), -6),
     (dict(scale=0.0), -7), (dict(scale=-0.5), -7), (dict(scale=float("inf")), -7), (dict(scale=float("nan")), -7),
     (dict(q=P + 8), -8), (dict(o=P + 2), -8), (dict(lse=P + 4), -8),
@@ -94,7 +94,7 @@ def test_fp8_validation_errors(lib):
     assert call(v8=None) == -1
     assert call(Hkv=3) == -3
     assert call(d=80) == -4
-    assert call(Sk=9) == -5
+    assert call(Sq=9) == -5
     assert call(dq=0.0) == -7 and call(dk=float("nan")) == -7 and call(dv=-1.0) == -7
     assert call(scale=float("inf")) == -7
     assert call(k8=P + 1) == -8

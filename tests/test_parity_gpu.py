@@ -74,6 +74,15 @@ def test_cross_attention_lengths(gpu, dtype, Sq, Sk):
     _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, 128 if dtype != "f32" else 64, dtype, False, seed=Sq * 7 + Sk))
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128), ("fp8", 64),
+                                     ("fp8", 128)])
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 300), (5, 64), (77, 200), (130, 257), (256, 1000), (300, 301)])
+def test_causal_queries_are_the_last_positions(gpu, dtype, d, Sq, Sk):
+    """Causal with Sq < Sk: query i sees keys j <= i + (Sk - Sq) (new queries against a longer key
+    sequence); single-query decode shapes included. Element-wise against the oracle, lse on."""
+    _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, d, dtype, True, seed=5000 + Sq * 3 + Sk, want_lse=True))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_batch_and_heads_mapping(gpu, d):
     """Several batches and GQA groups at once, causal, lse on."""
@@ -224,7 +233,7 @@ def test_errors_raise_through_python(gpu):
     z = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
     z9 = torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sdpa.AttnError, match="ATTN_ERR_CAUSAL_SHAPE"):
-        sdpa.fwd(z, z9, z9, causal=True)
+        sdpa.fwd(z9, z, z, causal=True)
 
 
 # ----------------------------------------------- full-size workloads, sampled rows
