@@ -15,9 +15,10 @@ Timing mirrors the codelab's benchmark helper ("Accelerate attention on GPU
 with cuDNN and TransformerEngine", section 8: warm-up calls first, inputs
 already on the device, warm caches), with device events instead of host time.
 
-Other modes (for profiling runs):
+Other modes:
     --no-cpu-baseline        skip the oracle timing
     --copy-calibration MIB   run a plain device copy of MIB MiB (to calibrate HBM byte counters)
+    --sweep                  the codelab's own benchmark shapes (one JSON line per shape, see sweep_shapes)
 """
 
 from __future__ import annotations
@@ -151,6 +152,69 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
+def sweep_shapes():
+    """The benchmark cells of the codelab ("Accelerate attention on GPU with cuDNN
+    and TransformerEngine"): its base shape is B=4, N=8 heads, head dim 64
+    (section 3); section 8 sweeps the sequence length over 64..1024 and the batch
+    over 1..16 at T=256, unmasked, in fp32 and bf16; the TransformerEngine cell
+    sweeps causal bf16 over T=128..2048; the FP8 cell runs causal attention at
+    T=2048. Seeds follow the cells' key numbers (sl, bs + 100, sl + 1000, 9000).
+    Returns (sweep name, Workload) pairs in the library's [B, H, S, d] layout."""
+    import sdpa_inputs
+    B, N, H = 4, 8, 64
+    out = []
+    for dtype in ("f32", "bf16"):
+        for sl in (64, 128, 256, 512, 1024):
+            out.append(("seq_len", sdpa_inputs.custom(B, N, N, sl, sl, H, dtype, False, seed=sl,
+                                                      name=f"seq_len_{dtype}_b{B}_t{sl}")))
+        for bs in (1, 2, 4, 8, 16):
+            out.append(("batch", sdpa_inputs.custom(bs, N, N, 256, 256, H, dtype, False, seed=bs + 100,
+                                                    name=f"batch_{dtype}_b{bs}_t256")))
+    for sl in (128, 256, 512, 1024, 2048):
+        out.append(("causal_bf16", sdpa_inputs.custom(B, N, N, sl, sl, H, "bf16", True, seed=sl + 1000,
+                                                      name=f"causal_bf16_b{B}_t{sl}")))
+    out.append(("fp8", sdpa_inputs.custom(B, N, N, 2048, 2048, H, "fp8", True, seed=9000, name=f"fp8_causal_b{B}_t2048")))
+    return out
+
+
+def run_sweep(warmup: int = 2, repeats: int = 20) -> int:
+    """Time every sweep shape like the codelab's helper (warm-up calls, then the
+    median of the timed calls), with HIP events on the launch stream."""
+    import torch
+    import sdpa_inputs
+    import scaled_dot_product_18_amd as sdpa
+    sdpa.require_library()
+    stream = torch.cuda.current_stream()
+    for sweep, w in sweep_shapes():
+        inp = sdpa_inputs.make_inputs(w)
+        dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
+
+        def call():
+            if w.dtype == "fp8":
+                sdpa.fwd_fp8(dev["q"], dev["k"], dev["v"], inp["descale_q"], inp["descale_k"], inp["descale_v"],
+                             causal=w.causal, scale=w.scale)
+            else:
+                sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(repeats):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        med = sorted(times)[len(times) // 2]
+        print(json.dumps({"sweep": sweep, "workload": w.name, "B": w.B, "T": w.Sq, "N": w.Hq, "H": w.d,
+                          "dtype": w.dtype, "causal": w.causal, "ms_median": round(med, 5),
+                          "tflops": round(w.flops() / (med * 1e-3) / 1e12, 3),
+                          "tokens_per_s": round(w.B * w.Sq / (med * 1e-3), 1)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +224,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--sweep", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -174,6 +239,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return 0
+    if args.sweep:
+        return run_sweep()
 
     import sdpa_inputs
     import scaled_dot_product_18_amd as sdpa
