@@ -32,8 +32,9 @@
 //    maximum exceeds it by more than 2^8 in probability units; otherwise the
 //    stale maximum is kept. Softmax is invariant to the reference point, so
 //    this is exact, and it removes the per-tile rescale of the accumulator;
-//  * row sums are taken with v_dot2_f32_bf16 on the bf16 probabilities the
-//    MFMA consumes, so numerator and normaliser use the same values;
+//  * 64-key tiles keep a workgroup's double-buffered K and V at 32 KB of LDS,
+//    so VGPRs, not LDS, bound the resident workgroups per CU;
+//  * row sums add the fp32 probabilities in four independent partial sums;
 //  * causal workgroups stop at the diagonal, run heaviest first, and query
 //    heads that share a KV head are placed on the same XCD (same L2).
 #include "kernel_common.h"
@@ -48,10 +49,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int D>
 struct Bf16Cfg {
   static constexpr int BM = 128;             // query rows per workgroup
-  static constexpr int BN = 8192 / D;        // keys per tile: 64 (d=128), 128 (d=64)
+  static constexpr int BN = 64;              // keys per tile (32 KB of LDS per workgroup at d=64)
   static constexpr int RB = D * 2;           // bytes per K/V row
   static constexpr int CH = RB / 16;         // 16-byte chunks per row
-  static constexpr int TILE = BN * RB;       // bytes of a K (or V) tile: 16 KB
+  static constexpr int TILE = BN * RB;       // bytes of a K (or V) tile
   static constexpr int STAGE = 2 * TILE;     // K tile then V tile
   static constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide DMA instructions per tensor per wave
   static constexpr int ROWS_PER_DMA = 1024 / RB;
@@ -59,7 +60,7 @@ struct Bf16Cfg {
   static constexpr int KC = BN / 16;         // 16-key chunks (K depth of P.V)
   static constexpr int DB = D / 32;          // 32-wide output blocks
   static constexpr int QS = D / 16;          // MFMAs per 32x32 score block
-  static_assert(DMA == 4, "4 waves x 4 DMA instructions cover a 16 KB tile");
+  static_assert(DMA * 4 * 1024 == TILE, "4 waves x DMA instructions cover a tile");
 };
 
 // Chunk swizzle of K rows: lanes 0..15 of an operand read hit 16 different rows
@@ -80,18 +81,19 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unl
 
 constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource: 32-bit data format (gfx9 family)
 
-// This wave's 4 wave-wide loads of one K or V tile, HBM -> LDS (lane l of load
+// This wave's NLOAD wave-wide loads of one K or V tile, HBM -> LDS (lane l of load
 // t fills the 16 bytes at dst + 1024 t + 16 l). The tile is read through a raw
 // buffer that starts at its first row and ends at the end of the sequence, so
 // rows at or past Sk fall outside the buffer and load as zeros. Called from
 // the kernel body, not from a lambda: the host pass rejects a device function
 // called from a lambda in a kernel template and then drops the launch stub.
+template <int NLOAD>
 __device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int seq_bytes,
                                          const unsigned* off, unsigned char* dst) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(base + kt * tile_bytes), (short)0, seq_bytes - kt * tile_bytes, kBufferConfig);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < NLOAD; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
 }
 
@@ -147,13 +149,13 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   const bool wave_active = qw < p.Sq;
   const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BN + 1) : n_tiles);
 
-  // ---- DMA assignment: wave w writes 1 KB blocks 4w..4w+3 of each tile -----
-  // 16-byte slot s = 64*(4w+t) + lane holds row s / CH, physical chunk s % CH.
+  // ---- DMA assignment: wave w writes 1 KB blocks DMA*w .. DMA*w+DMA-1 of each tile
+  // 16-byte slot s = 64*(DMA*w+t) + lane holds row s / CH, physical chunk s % CH.
   unsigned kdma_off[C::DMA], vdma_off[C::DMA];
   const int dma_pchunk = lane % C::CH;
 #pragma unroll
   for (int t = 0; t < C::DMA; ++t) {
-    const int row = (64 * (4 * wave + t) + lane) / C::CH;
+    const int row = (64 * (C::DMA * wave + t) + lane) / C::CH;
     kdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ k_swizzle<D>(row));
     vdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ v_swizzle<D>(row));
   }
@@ -186,8 +188,6 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   float m_run = -INFINITY;  // reference maximum, log2 units of the scaled score
   float l_run = 0.f;        // this lane's share of the normaliser
   const float c = p.qk_scale_log2;
-  typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(bf16_t)1.0f, (bf16_t)1.0f};
 
   auto compute_tile = [&](int kt, const unsigned char* stage) {
     const int kv0 = kt * C::BN;
@@ -234,8 +234,11 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
       for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
     }
 
-    // P^T operand: chunk kc = 2kb + j, element e <-> key 16kc + 8(e/4) + 4g + e%4
+    // P^T operand: chunk kc = 2kb + j, element e <-> key 16kc + 8(e/4) + 4g + e%4.
+    // The row sum adds the unrounded fp32 probabilities (v_dot2 on the packed
+    // bf16 values would stall the matrix core).
     u32x4 pf[C::KC];
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -245,10 +248,11 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
           const int r = 8 * j + 2 * e2;
           const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_run));
           const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_run));
-          const uint32_t w = pack_bf16x2(p0, p1);
-          pf[2 * kb + j][e2] = w;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l_run, false);
+          pf[2 * kb + j][e2] = pack_bf16x2(p0, p1);
+          lsum[e2] += p0;
+          lsum[e2] += p1;
         }
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // O^T += V^T . P^T
 #pragma unroll
@@ -266,21 +270,21 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   // ---- main loop: DMA of tile kt+1 overlaps compute of tile kt --------------
   const int kv_bytes = p.Sk * C::RB;
   if (n_tiles > 0) {
-    dma_tile(kbase, C::TILE, 0, kv_bytes, kdma_off, smem0 + 4096 * wave);
-    dma_tile(vbase, C::TILE, 0, kv_bytes, vdma_off, smem0 + C::TILE + 4096 * wave);
+    dma_tile<C::DMA>(kbase, C::TILE, 0, kv_bytes, kdma_off, smem0 + 1024 * C::DMA * wave);
+    dma_tile<C::DMA>(vbase, C::TILE, 0, kv_bytes, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
   }
   __syncthreads();
   for (int kt = 0; kt < n_tiles; kt += 2) {
     if (kt + 1 < n_tiles) {
-      dma_tile(kbase, C::TILE, kt + 1, kv_bytes, kdma_off, smem1 + 4096 * wave);
-      dma_tile(vbase, C::TILE, kt + 1, kv_bytes, vdma_off, smem1 + C::TILE + 4096 * wave);
+      dma_tile<C::DMA>(kbase, C::TILE, kt + 1, kv_bytes, kdma_off, smem1 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, C::TILE, kt + 1, kv_bytes, vdma_off, smem1 + C::TILE + 1024 * C::DMA * wave);
     }
     if (kt < wave_tiles) compute_tile(kt, smem0);
     __syncthreads();
     if (kt + 1 >= n_tiles) break;
     if (kt + 2 < n_tiles) {
-      dma_tile(kbase, C::TILE, kt + 2, kv_bytes, kdma_off, smem0 + 4096 * wave);
-      dma_tile(vbase, C::TILE, kt + 2, kv_bytes, vdma_off, smem0 + C::TILE + 4096 * wave);
+      dma_tile<C::DMA>(kbase, C::TILE, kt + 2, kv_bytes, kdma_off, smem0 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, C::TILE, kt + 2, kv_bytes, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
     }
     if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem1);
     __syncthreads();
