@@ -41,6 +41,8 @@
 #ifndef SDPA18_ATTN_H
 #define SDPA18_ATTN_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -65,7 +67,9 @@ enum {
   ATTN_ERR_DTYPE = -6,         /* dtype is not an attn_dtype_t value                    */
   ATTN_ERR_SCALE = -7,         /* scale or a descale is not finite and > 0              */
   ATTN_ERR_ALIGN = -8,         /* a base pointer is not 16-byte aligned                 */
-  ATTN_ERR_LAUNCH = -9         /* the HIP runtime rejected the kernel launch            */
+  ATTN_ERR_LAUNCH = -9,        /* the HIP runtime rejected the kernel launch            */
+  ATTN_ERR_WORKSPACE = -10,    /* split-KV workspace missing, misaligned or too small   */
+  ATTN_ERR_SPLITS = -11        /* num_splits outside [0, 128]                           */
 };
 
 /*
@@ -106,6 +110,51 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                  float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/*
+ * attn_fwd_splitkv -- the same operation as attn_fwd, computed for few
+ * queries against a long key sequence (decoding against a KV cache: Sq of 1
+ * to a few dozen, Sk in the thousands; the codelab's section 9 shares KV heads
+ * between query heads, and its closing next steps point at such shapes). The
+ * rows of the G = Hq / Hkv query heads that share a KV head are computed
+ * together, and the keys of each KV head are cut into num_splits chunks that
+ * run in parallel. Each chunk yields a normalised partial output and its
+ * log-sum-exp; a second kernel merges them exactly (softmax over the union of
+ * chunks: weights exp(lse_s - max lse), the rescaling step of the online
+ * softmax in the article's section 3). Results agree with attn_fwd up to
+ * rounding.
+ *
+ *   q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream  as attn_fwd.
+ *   dtype        ATTN_BF16 only (ATTN_ERR_DTYPE otherwise).
+ *   num_splits   0 = the library's choice (enough chunks to fill the GPU, at
+ *                least 256 keys each), else at most 128 chunks; a chunk holds
+ *                a multiple of 32 keys, so fewer may run (see the plan call).
+ *   workspace    device memory owned by the caller, 16-byte aligned, of at
+ *                least the size attn_fwd_splitkv_plan reports for the same
+ *                sizes and num_splits; may be NULL when that size is 0 (one
+ *                chunk). It holds fp32 partial outputs [B*Hq*Sq][splits][d]
+ *                then their base-2 log-sum-exps [B*Hq*Sq][splits]; contents
+ *                on entry are ignored and on return are unspecified. Two
+ *                calls in flight at once need two workspaces.
+ *
+ * Returns ATTN_OK or a negative status; ATTN_ERR_WORKSPACE if the workspace
+ * is missing, misaligned or too small, ATTN_ERR_SPLITS if num_splits is
+ * outside [0, 128].
+ */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     float scale, int causal, int dtype, int num_splits,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_fwd_splitkv_plan -- host-only query: the number of key chunks
+ * attn_fwd_splitkv will run for these sizes and num_splits (*splits_used)
+ * and the workspace bytes it needs (*workspace_bytes, 0 for one chunk).
+ * Either output pointer may be NULL. Enqueues nothing. Returns ATTN_OK or the
+ * status attn_fwd_splitkv would return for these sizes.
+ */
+int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits,
+                          int* splits_used, size_t* workspace_bytes);
 
 /* attn_strerror -- static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -22,7 +22,8 @@ import torch
 from . import _lib
 from ._lib import AttnError, ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8", "AttnError", "library_path", "version", "require_library"]
+__all__ = ["fwd", "fwd_fp8", "fwd_splitkv", "splitkv_plan", "AttnError", "library_path", "version",
+           "require_library"]
 
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
@@ -105,6 +106,45 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: flo
                                  lse.data_ptr() if lse is not None else None,
                                  B, Hq, Hkv, Sq, Sk, d, scale, causal,
                                  float(descale_q), float(descale_k), float(descale_v), stream))
+    return out, lse
+
+
+def splitkv_plan(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, num_splits: int = 0) -> Tuple[int, int]:
+    """(key chunks, workspace bytes) that :func:`fwd_splitkv` uses for these sizes."""
+    st, n, nbytes = _lib.attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits)
+    _lib.check(st)
+    return n, nbytes
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                scale: Optional[float] = None, want_lse: bool = False, num_splits: int = 0,
+                out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Split-KV attention forward for bfloat16 inputs: the same result as :func:`fwd`,
+    computed for few queries against many keys (decoding against a KV cache).
+
+    The keys are cut into ``num_splits`` chunks (0 = the library's choice) that
+    run in parallel and merge exactly through their log-sum-exps. ``workspace``
+    (a device tensor of at least ``splitkv_plan(...)[1]`` bytes) is allocated
+    here when not given. Other arguments as :func:`fwd`.
+    """
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"fwd_splitkv takes bfloat16 q/k/v, got {q.dtype}/{k.dtype}/{v.dtype}")
+    B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, B, Hq, Sq, d, q.dtype, want_lse, out, lse_out)
+    _, nbytes = splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _lib.check(_lib.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_BF16, int(num_splits),
+                                     ws_ptr, ws_bytes, stream))
     return out, lse
 
 

@@ -27,6 +27,8 @@ STATUS = {
     -7: "ATTN_ERR_SCALE",
     -8: "ATTN_ERR_ALIGN",
     -9: "ATTN_ERR_LAUNCH",
+    -10: "ATTN_ERR_WORKSPACE",
+    -11: "ATTN_ERR_SPLITS",
 }
 
 _lock = threading.Lock()
@@ -56,6 +58,11 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, vp]
         lib.attn_fwd_fp8.restype = i
+        sz = ctypes.c_size_t
+        lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+        lib.attn_fwd_splitkv.restype = i
+        lib.attn_fwd_splitkv_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(sz)]
+        lib.attn_fwd_splitkv_plan.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -81,3 +88,18 @@ def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, strea
 def attn_fwd_fp8(q8, k8, v8, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dq, dk, dv, stream) -> int:
     """Raw call with integer pointers; returns the status code."""
     return load().attn_fwd_fp8(q8, k8, v8, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dq, dk, dv, stream)
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, num_splits, ws, ws_bytes,
+                     stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dtype, num_splits,
+                                   ws, ws_bytes, stream)
+
+
+def attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits):
+    """(status, splits_used, workspace_bytes) of the host-only plan query."""
+    n = ctypes.c_int(0)
+    nbytes = ctypes.c_size_t(0)
+    st = load().attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits, ctypes.byref(n), ctypes.byref(nbytes))
+    return st, n.value, nbytes.value

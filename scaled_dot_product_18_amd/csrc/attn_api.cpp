@@ -62,6 +62,53 @@ sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+constexpr int kMaxSplits = 128;
+
+// Checks of attn_fwd_splitkv_plan and attn_fwd_splitkv beyond the shared ones.
+int validate_split_sizes(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (num_splits < 0 || num_splits > kMaxSplits) return ATTN_ERR_SPLITS;
+  const int64_t ctiles = ((int64_t)(Hq / Hkv) * Sq + 31) / 32;
+  if ((int64_t)Sq * d * 4 >= INT32_MAX || (int64_t)Sk * d * 4 >= INT32_MAX ||
+      ctiles * B * Hkv * kMaxSplits >= INT32_MAX || (int64_t)B * Hq * Sq >= INT32_MAX)
+    return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+// Key chunking of the split-KV path. num_splits = 0 picks enough chunks for
+// one resident round of workgroups on the 256 CUs (one workgroup per CU at
+// d = 128, where a workgroup holds 128 KB of LDS; two at d = 64), keeping at
+// least 256 keys (two 32-key blocks per wave) in a chunk. Chunks hold a
+// multiple of 32 keys; the count is what remains after rounding, so no chunk
+// is empty.
+struct SplitPlan {
+  int n_splits, chunk, n_ctiles;
+  size_t workspace;
+};
+SplitPlan plan_splits(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits) {
+  SplitPlan pl;
+  pl.n_ctiles = (int)(((int64_t)(Hq / Hkv) * Sq + 31) / 32);
+  const int max_blocks = (Sk + 31) / 32;
+  int ns;
+  if (num_splits > 0) {
+    ns = num_splits < max_blocks ? num_splits : max_blocks;
+  } else {
+    const int64_t items = (int64_t)B * Hkv * pl.n_ctiles;
+    const int64_t target = d == 128 ? 256 : 512;
+    int64_t want = (target + items - 1) / items;
+    const int64_t by_len = (Sk + 255) / 256;
+    if (want > by_len) want = by_len;
+    if (want > kMaxSplits) want = kMaxSplits;
+    ns = want < 1 ? 1 : (int)want;
+  }
+  pl.chunk = ((Sk + ns - 1) / ns + 31) / 32 * 32;
+  pl.n_splits = (Sk + pl.chunk - 1) / pl.chunk;
+  pl.workspace = pl.n_splits > 1 ? (size_t)B * Hq * Sq * pl.n_splits * (size_t)(d + 1) * sizeof(float) : 0;
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +148,39 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, f
   return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
+int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits, int* splits_used,
+                          size_t* workspace_bytes) {
+  const int st = validate_split_sizes(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (st != ATTN_OK) return st;
+  const SplitPlan pl = plan_splits(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (splits_used != nullptr) *splits_used = pl.n_splits;
+  if (workspace_bytes != nullptr) *workspace_bytes = pl.workspace;
+  return ATTN_OK;
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int d, float scale, int causal, int dtype, int num_splits, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  st = validate_split_sizes(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
+  const SplitPlan pl = plan_splits(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (pl.workspace > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < pl.workspace))
+    return ATTN_ERR_WORKSPACE;
+  sdpa18::SplitParams sp;
+  sp.a = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, 128);
+  const size_t rows = (size_t)B * Hq * Sq;
+  sp.part_o = pl.workspace > 0 ? static_cast<float*>(workspace) : nullptr;
+  sp.part_lse = pl.workspace > 0 ? static_cast<float*>(workspace) + rows * pl.n_splits * (size_t)d : nullptr;
+  sp.n_splits = pl.n_splits;
+  sp.chunk = pl.chunk;
+  sp.n_ctiles = pl.n_ctiles;
+  return launch_status(sdpa18::launch_attn_splitkv_bf16(sp, d, causal != 0, stream));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
@@ -113,10 +193,12 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or smaller than attn_fwd_splitkv_plan requires";
+    case ATTN_ERR_SPLITS: return "num_splits must be in [0, 128]";
     default: return "unknown status";
   }
 }
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 200; }
 
 }  // extern "C"

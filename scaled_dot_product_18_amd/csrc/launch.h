@@ -31,4 +31,20 @@ hipError_t launch_attn_fp8_pp(const AttnParams& p, bool causal, hipStream_t stre
 // fp32 inputs and output; d in {64, 128}.
 hipError_t launch_attn_f32(const AttnParams& p, int d, bool causal, hipStream_t stream);
 
+// Split-KV forward: the keys of each KV head are cut into n_splits chunks of
+// `chunk` keys (a multiple of 32), one workgroup per (column tile, batch, KV
+// head, chunk); a column tile packs 32 (query head of the group, query) rows.
+struct SplitParams {
+  AttnParams a;     // n_qtiles and xcd_remap are unused
+  float* part_o;    // [B*Hq*Sq][n_splits][d] normalised partial outputs (n_splits > 1)
+  float* part_lse;  // [B*Hq*Sq][n_splits] base-2 log-sum-exp of the scaled scores of each chunk
+  int n_splits;
+  int chunk;
+  int n_ctiles;     // ceil(group * Sq / 32)
+};
+
+// bf16 inputs and output, d in {64, 128}; with n_splits > 1 a second kernel
+// merges the chunks into o and lse.
+hipError_t launch_attn_splitkv_bf16(const SplitParams& sp, int d, bool causal, hipStream_t stream);
+
 }  // namespace sdpa18

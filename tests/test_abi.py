@@ -32,7 +32,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _header_functions() == ["attn_fwd", "attn_fwd_fp8", "attn_strerror", "attn_version"]
+    assert _header_functions() == ["attn_fwd", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_fwd_splitkv_plan",
+                                   "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -98,6 +99,56 @@ def test_fp8_validation_errors(lib):
     assert call(dq=0.0) == -7 and call(dk=float("nan")) == -7 and call(dv=-1.0) == -7
     assert call(scale=float("inf")) == -7
     assert call(k8=P + 1) == -8
+
+
+def test_splitkv_validation_errors(lib):
+    f = lib.load().attn_fwd_splitkv
+    ok = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=1, Sq=1, Sk=4096, d=128, scale=0.1, causal=0,
+              dtype=1, ns=8, ws=P, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"],
+                 a["scale"], a["causal"], a["dtype"], a["ns"], a["ws"], a["ws_bytes"], None)
+
+    assert call(dtype=0) == -6 and call(dtype=2) == -6
+    assert call(o=None) == -1
+    assert call(Sq=0) == -2
+    assert call(Hkv=3) == -3
+    assert call(d=96) == -4
+    assert call(causal=1, Sq=4097) == -5
+    assert call(scale=0.0) == -7
+    assert call(q=P + 4) == -8
+    assert call(ns=-1) == -11 and call(ns=129) == -11
+    assert call(ws=None) == -10
+    assert call(ws=P + 8) == -10
+    assert call(ws_bytes=1000) == -10
+    st, n, nbytes = lib.attn_fwd_splitkv_plan(1, 4, 1, 1, 4096, 128, 8)
+    assert (st, n) == (0, 8) and nbytes == 4 * 8 * 129 * 4
+    assert call(ws_bytes=nbytes - 1) == -10
+
+
+@pytest.mark.parametrize("sizes,ns", [((4, 32, 8, 1, 4096, 128), 0), ((4, 32, 32, 1, 4096, 128), 0),
+                                      ((1, 32, 8, 16, 32768, 128), 0), ((32, 12, 12, 196, 196, 64), 0),
+                                      ((1, 1, 1, 1, 1, 64), 0), ((2, 8, 2, 5, 1500, 128), 7),
+                                      ((2, 8, 2, 5, 1500, 128), 128), ((1, 2, 1, 3, 100, 64), 128)])
+def test_splitkv_plan(lib, sizes, ns):
+    """Chunk counts: within [1, 128], within ceil(Sk / 32) (a chunk holds a multiple of 32
+    keys), no empty chunk, at most what was asked for; the workspace holds fp32 partial
+    outputs and log-sum-exps of every row and chunk, none for one chunk."""
+    B, Hq, Hkv, Sq, Sk, d = sizes
+    st, n, nbytes = lib.attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, ns)
+    assert st == 0
+    assert 1 <= n <= min(128, -(-Sk // 32))
+    if ns:
+        assert n <= ns
+    chunk = -(-(-(-Sk // max(n, 1))) // 32) * 32
+    assert (n - 1) * chunk < Sk <= n * chunk or n == 1
+    assert nbytes == (B * Hq * Sq * n * (d + 1) * 4 if n > 1 else 0)
+    # The default fills the GPU: at least 256 workgroups or 256 keys per chunk.
+    if ns == 0:
+        items = B * Hkv * -(-(Hq // Hkv) * Sq // 32)
+        assert items * n >= 256 or n == min(128, -(-Sk // 256)) or n == -(-Sk // 32)
 
 
 def test_python_wrapper_rejects_cpu_tensors():

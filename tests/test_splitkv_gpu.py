@@ -1,0 +1,104 @@
+"""GPU parity of the split-KV forward (attn_fwd_splitkv) against the fp64 oracle.
+
+Decode shapes: one or a few queries against many keys, the query heads of a
+GQA/MQA group packed together, keys cut into chunks merged through their
+log-sum-exps. Every case is compared element by element with the full oracle
+at the bf16 tolerances of the fused forward (O 2e-2, lse 4e-3); the key counts
+span one block, block edges (31/32/33), ragged tails and several chunks.
+"""
+
+import itertools
+
+import pytest
+import torch
+
+import sdpa_inputs
+from parity_util import check_full, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, num_splits=0, workspace=None):
+    import scaled_dot_product_18_amd as sdpa
+    n, nbytes = sdpa.splitkv_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, num_splits)
+    log(f"[splitkv] {w.name} num_splits={num_splits} -> {n} chunks, {nbytes} workspace bytes")
+    inp = sdpa_inputs.make_inputs(w)
+    dev = to_device(inp)
+    o, lse = sdpa.fwd_splitkv(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, want_lse=True,
+                              num_splits=num_splits, workspace=workspace)
+    torch.cuda.synchronize()
+    return check_full(w, inp, o, lse), inp, dev, o, lse
+
+
+DECODE_SK = [1, 31, 32, 33, 129, 300, 1000, 4097]
+GROUPS = [(8, 8), (8, 2), (8, 1), (32, 1)]
+
+
+@pytest.mark.parametrize("Sk,heads,d", list(itertools.product(DECODE_SK, GROUPS, (64, 128))))
+def test_single_query_decode(gpu, Sk, heads, d):
+    """Sq = 1 against Sk keys (causal and not: with one query the mask allows every key)."""
+    Hq, Hkv = heads
+    for causal in (False, True):
+        _run(sdpa_inputs.custom(2, Hq, Hkv, 1, Sk, d, "bf16", causal, seed=7000 + Sk + Hq * 7 + Hkv,
+                                want_lse=True))
+
+
+@pytest.mark.parametrize("Sq,Sk,heads,d", list(itertools.product([2, 3, 16, 64], [64, 333, 2048], [(8, 2), (32, 1)],
+                                                                   (64, 128))))
+def test_query_blocks_causal(gpu, Sq, Sk, heads, d):
+    """A few queries (speculative decoding, chunked prefill) with the bottom-right causal mask:
+    query i sees keys j <= i + Sk - Sq. Group x Sq spans one or several 32-column tiles."""
+    Hq, Hkv = heads
+    _run(sdpa_inputs.custom(1, Hq, Hkv, Sq, Sk, d, "bf16", True, seed=7500 + Sq * 11 + Sk, want_lse=True))
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 64, 128])
+def test_explicit_split_counts(gpu, num_splits):
+    """Every chunk count gives the same answer; counts above ceil(Sk / 32) are cut to that."""
+    for causal in (False, True):
+        _run(sdpa_inputs.custom(2, 8, 2, 5, 1500, 128, "bf16", causal, seed=7900 + num_splits, want_lse=True),
+             num_splits=num_splits)
+
+
+def test_agrees_with_fused_forward(gpu):
+    import scaled_dot_product_18_amd as sdpa
+    w = sdpa_inputs.custom(2, 16, 4, 8, 3000, 128, "bf16", True, seed=8100, want_lse=True)
+    _, inp, dev, o, lse = _run(w)
+    o2, lse2 = sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=True, scale=w.scale, want_lse=True)
+    torch.cuda.synchronize()
+    assert (o.float() - o2.float()).abs().max().item() <= 2e-2
+    assert (lse - lse2).abs().max().item() <= 4e-3
+
+
+def test_decode_at_serving_size(gpu):
+    """B4 Hq32 Hkv8 d128 against a 16K-key cache, one query per sequence: the library's own
+    chunking (several chunks per KV head), every output element checked."""
+    _run(sdpa_inputs.custom(4, 32, 8, 1, 16384, 128, "bf16", False, seed=8200, want_lse=True))
+
+
+def test_workspace_reused_across_calls(gpu):
+    """One caller workspace, two calls in a row (the second smaller): the second result owes
+    nothing to what the first left behind."""
+    import scaled_dot_product_18_amd as sdpa
+    _, nbytes = sdpa.splitkv_plan(2, 8, 2, 4, 4096, 128, 16)
+    ws = torch.full((nbytes,), 0x7f, dtype=torch.uint8, device="cuda")  # NaN-ish garbage as fp32
+    _run(sdpa_inputs.custom(2, 8, 2, 4, 4096, 128, "bf16", True, seed=8300, want_lse=True), num_splits=16,
+         workspace=ws)
+    _run(sdpa_inputs.custom(1, 4, 1, 2, 700, 64, "bf16", False, seed=8301, want_lse=True), num_splits=5,
+         workspace=ws)
+
+
+def test_errors_raise_through_python(gpu):
+    import scaled_dot_product_18_amd as sdpa
+    from scaled_dot_product_18_amd import AttnError
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 1, 4096, 128, dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(AttnError) as e:
+        sdpa.fwd_splitkv(q, k, k, num_splits=8, workspace=small)
+    assert e.value.status == -10
+    with pytest.raises(AttnError) as e:
+        sdpa.fwd_splitkv(q, k, k, num_splits=200)
+    assert e.value.status == -11
+    with pytest.raises(ValueError):
+        sdpa.fwd_splitkv(q.float(), k.float(), k.float())
