@@ -15,6 +15,12 @@ Timing mirrors the codelab's benchmark helper ("Accelerate attention on GPU
 with cuDNN and TransformerEngine", section 8: warm-up calls first, inputs
 already on the device, warm caches), with device events instead of host time.
 
+--workload takes any name of sdpa_inputs.WORKLOADS. The decode workload runs
+the split-KV path (one step = the chunk kernel plus the merge kernel); a
+workload whose arithmetic intensity is below the ridge point reports the HBM
+roofline (algorithmic bytes per launch over the launch time) instead of the
+matrix-core one.
+
 Other modes:
     --no-cpu-baseline        skip the oracle timing
     --copy-calibration MIB   run a plain device copy of MIB MiB (to calibrate HBM byte counters)
@@ -51,7 +57,8 @@ def log(msg: str) -> None:
 # Source file of each kernel family; its counter summaries are keyed on it.
 KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
                   "attn_fwd_fp8_pp_kernel": "attn_fwd_fp8_pp.hip",
-                  "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip"}
+                  "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip",
+                  "attn_fwd_splitkv_kernel": "attn_fwd_splitkv.hip"}
 SHARED_SOURCES = ("kernel_common.h", "launch.h", "attn_api.cpp")
 
 
@@ -68,6 +75,8 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def kernel_name(w) -> str:
+    if w.path == "splitkv":
+        return "attn_fwd_splitkv_kernel"
     if w.dtype == "bf16" and w.d == 128:
         return "attn_fwd_bf16_pp_kernel"
     if w.dtype == "fp8" and w.d == 128:
@@ -255,8 +264,16 @@ def main() -> int:
                       device="cuda")
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device="cuda") if w.want_lse else None
 
+    workspace = None
+    if w.path == "splitkv":
+        _, nbytes = sdpa.splitkv_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
     def step():
-        if w.dtype == "fp8":
+        if w.path == "splitkv":
+            sdpa.fwd_splitkv(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, out=out, lse_out=lse,
+                             workspace=workspace)
+        elif w.dtype == "fp8":
             sdpa.fwd_fp8(dev["q"], dev["k"], dev["v"], inp["descale_q"], inp["descale_k"], inp["descale_v"],
                          causal=w.causal, scale=w.scale, out=out, lse_out=lse)
         else:
@@ -296,6 +313,14 @@ def main() -> int:
         f"(median {per_launch[len(per_launch) // 2] * 1e3:.1f}, min {per_launch[0] * 1e3:.1f}), "
         f"host wall {t_wall / args.steps * 1e3:.1f} us/step")
 
+    # The roofline that bounds the workload: below the ridge point (peak FLOP/s
+    # over peak bytes/s) it is HBM bandwidth, above it the matrix cores.
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / w.hbm_bytes() < ridge:
+        bound, unit_r, peak_r = "hbm", "GB/s", PEAK_HBM_GBS
+        achieved_r = w.hbm_bytes() / (avg_launch_ms * 1e-3) / 1e9
+    else:
+        bound, unit_r, peak_r, achieved_r = "mfma", "TFLOP/s", peak, achieved
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -310,18 +335,18 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. N(0,1) q/k/v" + (", per-tensor amax e4m3fn" if w.dtype == "fp8" else ""),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
-                   "causal": w.causal, "lse": w.want_lse, "in_dtype": w.dtype,
+                   "causal": w.causal, "lse": w.want_lse, "in_dtype": w.dtype, "path": w.path,
                    "out_dtype": "f32" if w.dtype == "f32" else "bf16", "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "tokens_per_s": round(w.B * w.Sq / (ms_per_step * 1e-3), 1),
         "hbm_gbs_algorithmic": round(w.hbm_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "kernel": kernel_name(w),
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            "achieved": round(achieved_r, 2),
+            "peak": peak_r,
+            "unit": unit_r,
+            "frac": round(achieved_r / peak_r, 4),
             "traffic": traffic_from_profiles(w),
             "algorithmic_flop_per_launch": flops,
             "algorithmic_bytes_per_launch": w.hbm_bytes(),

@@ -5,12 +5,14 @@ tests. It holds no attention arithmetic: it draws N(0,1) tensors, rounds them
 to the storage dtype, and quantises fp8 inputs with a per-tensor amax scale.
 
 Workloads follow the pages' shapes:
-  * the five workloads below are the ones the fused kernel is measured and
+  * the first workloads below are the ones the fused kernel is measured and
     checked on (single fp32 head; ViT-B/16 token count 196 with 12 heads of
     64 -- "Self-attention, CUDA kernels and FlashAttention", section 1;
     causal bf16 MHA; causal GQA/MQA with shared KV heads -- codelab
     "Accelerate attention on GPU with cuDNN and TransformerEngine", section 9;
-    and a long causal fp8-e4m3 workload -- same codelab, section 10);
+    and a long causal fp8-e4m3 workload -- same codelab, section 10); the
+    last is a decode step (one query per sequence against a long KV cache,
+    GQA heads of section 9) for the split-KV path;
   * every draw is i.i.d. standard normal, as every input cell of the codelab
     is (sections 3, 8, 9, 10), and bf16 values are fp32 draws cast to bf16
     (section 6).
@@ -51,6 +53,7 @@ class Workload:
     causal: bool
     seed: int
     want_lse: bool = False
+    path: str = "fused"  # "fused": attn_fwd / attn_fwd_fp8; "splitkv": attn_fwd_splitkv (decode shapes)
 
     @property
     def scale(self) -> float:
@@ -82,6 +85,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("causal_gqa_bf16_b4_hq32_hkv8_s4096_d128", 4, 32, 8, 4096, 4096, 128, "bf16", True, 42),
         Workload("causal_mqa_bf16_b4_hq32_hkv1_s4096_d128", 4, 32, 1, 4096, 4096, 128, "bf16", True, 42),
         Workload("causal_fp8_b1_h32_s16384_d128", 1, 32, 32, 16384, 16384, 128, "fp8", True, 9000),
+        # One new token per sequence against a 32K-token KV cache, the GQA cell's head layout.
+        Workload("decode_gqa_bf16_b4_hq32_hkv8_sk32768_d128", 4, 32, 8, 1, 32768, 128, "bf16", False, 42,
+                 path="splitkv"),
     ]
 }
 

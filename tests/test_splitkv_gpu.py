@@ -76,6 +76,17 @@ def test_decode_at_serving_size(gpu):
     _run(sdpa_inputs.custom(4, 32, 8, 1, 16384, 128, "bf16", False, seed=8200, want_lse=True))
 
 
+def test_decode_benchmark_workload(gpu):
+    """The benchmark's decode step (B4 Hq32 Hkv8, one query against 32K keys, d128), launched
+    as the benchmark launches it; every output element and lse checked."""
+    w = sdpa_inputs.WORKLOADS["decode_gqa_bf16_b4_hq32_hkv8_sk32768_d128"]
+    assert w.path == "splitkv"
+    w = sdpa_inputs.custom(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.dtype, w.causal, w.seed, want_lse=True,
+                           name=w.name)
+    stats, *_ = _run(w)
+    log(f"  {stats}")
+
+
 def test_workspace_reused_across_calls(gpu):
     """One caller workspace, two calls in a row (the second smaller): the second result owes
     nothing to what the first left behind."""
