@@ -59,7 +59,7 @@ typedef enum {
 /* Status codes: 0 is success, every error is negative. */
 enum {
   ATTN_OK = 0,
-  ATTN_ERR_NULL = -1,          /* q, k, v or o is NULL                                  */
+  ATTN_ERR_NULL = -1,          /* a required pointer is NULL (q, k, v, o; see attn_bwd) */
   ATTN_ERR_SHAPE = -2,         /* a size is < 1, or the problem exceeds 32-bit indexing */
   ATTN_ERR_HEADS = -3,         /* Hq is not a multiple of Hkv                           */
   ATTN_ERR_HEADDIM = -4,       /* d is not 64 or 128                                    */
@@ -155,6 +155,47 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  */
 int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits,
                           int* splits_used, size_t* workspace_bytes);
+
+/*
+ * attn_bwd -- gradients of the attention forward (the backward pass the
+ * article "Self-attention, CUDA kernels and FlashAttention", section 3,
+ * describes: the attention weights are recomputed tile by tile from the
+ * forward's per-row log-sum-exp instead of being stored). For a loss L with
+ * dout = dL/dO:
+ *
+ *   P = exp(scale Q K^T - lse)  (masked pairs 0)    dV = P^T dout
+ *   dS = P * (dout V^T - rowsum(dout * O))          dQ = scale dS K
+ *   dK = scale dS^T Q
+ *
+ * summed over the query heads that share a KV head (GQA/MQA). The mask, the
+ * head mapping and the layouts are those of attn_fwd.
+ *
+ *   q, k, v   the forward's inputs; o, lse its outputs (lse is required);
+ *   dout      dL/dO, layout of o;
+ *   dq        output, layout of q; dk, dv outputs, layout of k / v. Every
+ *             element is written (a KV head's gradient is the sum over its
+ *             query heads, computed without atomics);
+ *   dtype     ATTN_BF16 only: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse;
+ *   workspace device memory owned by the caller, 16-byte aligned, at least
+ *             attn_bwd_workspace_size bytes (B*Hq*Sq floats: the per-row
+ *             rowsum(dout * O)); contents on entry ignored, unspecified on
+ *             return; two calls in flight need two workspaces.
+ *   Other arguments as attn_fwd.
+ *
+ * Returns ATTN_OK or a negative status: ATTN_ERR_NULL if any of q, k, v, o,
+ * dout, lse, dq, dk, dv is NULL, ATTN_ERR_WORKSPACE for a missing, misaligned
+ * or short workspace, the other codes as attn_fwd.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d,
+             float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_bwd_workspace_size -- host-only: the workspace bytes attn_bwd needs
+ * for these sizes (*workspace_bytes, may be NULL). Returns ATTN_OK or the
+ * size error attn_bwd would return. */
+int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes);
 
 /* attn_strerror -- static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

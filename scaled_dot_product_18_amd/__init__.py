@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8", "fwd_splitkv", "splitkv_plan", "AttnError", "library_path", "version",
+__all__ = ["fwd", "fwd_fp8", "fwd_splitkv", "splitkv_plan", "bwd", "AttnError", "library_path", "version",
            "require_library"]
 
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
@@ -146,6 +146,44 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
                                      B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_BF16, int(num_splits),
                                      ws_ptr, ws_bytes, stream))
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
+        workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv) of the attention forward for bfloat16 tensors.
+
+    ``o`` and ``lse`` are what :func:`fwd` returned for (q, k, v) with
+    ``want_lse=True`` and the same ``causal`` and ``scale``; ``dout`` is the
+    gradient of the loss with respect to ``o``. dk and dv have k's shape (with
+    GQA/MQA they sum over the query heads that share a KV head). ``workspace``
+    (B*Hq*Sq float32) is allocated here when not given.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"bwd takes bfloat16 tensors, {name} is {t.dtype}")
+    B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape on q's device")
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [B, Hq, Sq] tensor fwd returned")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st, nbytes = _lib.attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+    _lib.check(st)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _lib.check(_lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                             B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_BF16,
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream))
+    return dq, dk, dv
 
 
 def require_library() -> None:

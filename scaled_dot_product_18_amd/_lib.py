@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
         lib.attn_fwd_splitkv.restype = i
         lib.attn_fwd_splitkv_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(sz)]
         lib.attn_fwd_splitkv_plan.restype = i
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+        lib.attn_bwd.restype = i
+        lib.attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_bwd_workspace_size.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -103,3 +107,17 @@ def attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits):
     nbytes = ctypes.c_size_t(0)
     st = load().attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits, ctypes.byref(n), ctypes.byref(nbytes))
     return st, n.value, nbytes.value
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, ws, ws_bytes,
+             stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dtype, ws,
+                           ws_bytes, stream)
+
+
+def attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d):
+    """(status, workspace_bytes) of the host-only size query."""
+    nbytes = ctypes.c_size_t(0)
+    st = load().attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d, ctypes.byref(nbytes))
+    return st, nbytes.value

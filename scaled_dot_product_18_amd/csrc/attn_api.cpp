@@ -181,10 +181,56 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   return launch_status(sdpa18::launch_attn_splitkv_bf16(sp, d, causal != 0, stream));
 }
 
+int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (workspace_bytes != nullptr) *workspace_bytes = (size_t)B * Hq * Sq * sizeof(float);
+  return ATTN_OK;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+             int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)((Sk + 127) / 128) * B * Hkv >= INT32_MAX) return ATTN_ERR_SHAPE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
+  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
+  const size_t need = (size_t)B * Hq * Sq * sizeof(float);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  sdpa18::BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.o = o;
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.delta = static_cast<float*>(workspace);
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.B = B;
+  bp.Hq = Hq;
+  bp.Hkv = Hkv;
+  bp.Sq = Sq;
+  bp.Sk = Sk;
+  bp.group = Hq / Hkv;
+  bp.causal_off = causal ? Sk - Sq : 0;
+  bp.scale = scale;
+  bp.qk_scale_log2 = scale * kLog2e;
+  bp.n_qtiles = (Sq + 127) / 128;
+  bp.n_ktiles = (Sk + 127) / 128;
+  return launch_status(sdpa18::launch_attn_bwd_bf16(bp, d, causal != 0, stream));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
-    case ATTN_ERR_NULL: return "q, k, v or o is a null pointer";
+    case ATTN_ERR_NULL: return "a required pointer (q, k, v, o; for attn_bwd also dout, lse, dq, dk, dv) is null";
     case ATTN_ERR_SHAPE: return "a size is < 1 or the problem exceeds 32-bit indexing";
     case ATTN_ERR_HEADS: return "Hq is not a multiple of Hkv";
     case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
@@ -193,7 +239,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
-    case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or smaller than attn_fwd_splitkv_plan requires";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or smaller than the size query reports";
     case ATTN_ERR_SPLITS: return "num_splits must be in [0, 128]";
     default: return "unknown status";
   }

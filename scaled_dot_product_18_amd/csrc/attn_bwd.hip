@@ -1,0 +1,478 @@
+// Attention backward pass for gfx950: dQ, dK, dV from Q, K, V, O, dO and the
+// forward's log-sum-exp, bf16 in and out, fp32 accumulation.
+//
+// The gradients are the chain rule through the forward's three steps (codelab
+// "Accelerate attention on GPU with cuDNN and TransformerEngine", section 4),
+// and the attention weights are recomputed tile by tile from the stored
+// per-row statistic instead of being kept (article "Self-attention, CUDA
+// kernels and FlashAttention", section 3):
+//   P = exp(scale Q K^T - lse)         dV = P^T dO         dP = dO V^T
+//   dS = P * (dP - delta), delta_i = sum_c dO_ic O_ic    (= sum_j P_ij dP_ij)
+//   dQ = scale dS K                    dK = scale dS^T Q
+// Three kernels on one stream:
+//  * attn_bwd_delta_kernel: delta for every query row (caller's workspace);
+//  * attn_bwd_dq_kernel: one workgroup per 128 queries of one (batch, query
+//    head), K/V tiles of 64 keys streamed HBM -> LDS as in the forward. The
+//    products are transposed as in the forward kernels (lane = query column):
+//    S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16, the per-row
+//    lse and delta are lane scalars, and dS^T rounded to bf16 is directly the
+//    B operand of dQ^T += K^T dS^T, whose K^T operand is a transposing LDS read;
+//  * attn_bwd_dkdv_kernel: one workgroup per 128 keys of one (batch, KV head),
+//    lane = key column: the wave's 32 K and V rows sit in VGPRs as the B
+//    operands of S = Q K^T and dP = dO V^T, Q and dO tiles of 64 queries stream
+//    through LDS for every query head of the KV head's group (so GQA/MQA sums
+//    over the group without atomics), and P, dS rounded to bf16 are the B
+//    operands of dV^T += dO^T P and dK^T += Q^T dS.
+// Under the causal mask (query i sees keys j <= i + Sk - Sq) tiles that see
+// nothing are skipped and only edge blocks are masked.
+#include "kernel_common.h"
+#include "launch.h"
+
+namespace sdpa18 {
+namespace bwd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource: 32-bit data format
+
+template <int D>
+struct Cfg {
+  static constexpr int RB = 2 * D;            // bytes per row
+  static constexpr int CH = RB / 16;          // 16-byte chunks per row
+  static constexpr int BT = 64;               // rows of a streamed tile
+  static constexpr int TILE = BT * RB;        // bytes of one streamed tile
+  static constexpr int DMA = TILE / 1024 / 4; // 1 KB wave-wide DMA loads per tile per wave
+  static constexpr int QS = D / 16;           // MFMAs per 32x32 product over d
+  static constexpr int DB = D / 32;           // 32-dim output blocks
+  static_assert(DMA * 4 * 1024 == TILE, "4 waves cover a tile");
+};
+
+// Chunk swizzles. Tiles read only row-wise (16 lanes at 16 rows, one chunk)
+// use row_swz; tiles also read through the transposing read (4 consecutive
+// rows, 32 bytes each) use tr_swz, which keeps those free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int row_swz(int row) {
+  return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int tr_swz(int row) {
+  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
+}
+
+// This wave's DMA loads of tile t of a row-major [rows, D] bf16 array, HBM ->
+// LDS (lane l of load i fills dst + 1024 i + 16 l). Rows at or past the end
+// fall outside the buffer's range and load as zeros.
+template <int NLOAD>
+__device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int t, int total_bytes,
+                                         const unsigned* off, unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + t * tile_bytes), (short)0, total_bytes - t * tile_bytes, kBufferConfig);
+#pragma unroll
+  for (int i = 0; i < NLOAD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * i), 16, off[i], 0, 0, 0);
+}
+
+// Offsets of the transposing reads that form a 32 (dim) x 16 (row) A operand
+// from a row-major tile: in each 16-lane group lane J reads 4 dims
+// [dbase + 4(J%4), +4) of row (row_base + J/4); the lo read covers rows
+// 16kc + 4g + J/4, the hi read the same rows + 8. Element e of the operand then
+// pairs with row 16kc + 8(e/4) + 4g + e%4, the row order of the packed
+// accumulator operands below.
+template <int D>
+__device__ __forceinline__ int tr_offset(int lane, int db) {
+  const int J = lane & 15;
+  const int g = lane >> 5;
+  const int r = 4 * g + (J >> 2);
+  const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
+  return r * (2 * D) + 16 * ((d >> 3) ^ tr_swz<D>(r)) + 2 * (d & 7);
+}
+
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* p, int rb) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * rb));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- delta
+// delta[row] = sum_c dO[row, c] * O[row, c]; D/8 lanes per row, 8 elements each.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void attn_bwd_delta_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)((const unsigned char*)p.o + row * (2 * D) + 16 * part);
+    const u32x4 b = *(const u32x4*)((const unsigned char*)p.dout + row * (2 * D) + 16 * part);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += bf16_lo(a[w]) * bf16_lo(b[w]) + bf16_hi(a[w]) * bf16_hi(b[w]);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && part == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_kernel(const BwdParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int BH = p.B * p.Hq;
+  const int qt_seq = blockIdx.x / BH;
+  const int rem = blockIdx.x - qt_seq * BH;
+  const int b = rem / p.Hq;
+  const int hq = rem - b * p.Hq;
+  const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_seq) : qt_seq;  // heaviest first under the mask
+  const int hk = hq / p.group;
+
+  const int q0 = qt * 128;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + i32;
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::RB;
+  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * C::RB;
+
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + 128 + p.causal_off) : p.Sk;
+  const int n_tiles = (kv_end + C::BT - 1) / C::BT;
+  const bool wave_active = qw < p.Sq;
+  const int wave_tiles =
+      !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BT + 1) : n_tiles);
+
+  // DMA slot s = 64 (DMA w + i) + lane: row s / CH, physical chunk s % CH.
+  unsigned kdma[C::DMA], vdma[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int r = (64 * (C::DMA * wave + i) + lane) / C::CH;
+    const int pc = lane % C::CH;
+    kdma[i] = r * C::RB + 16 * (pc ^ tr_swz<D>(r));   // K: row reads and transposing reads
+    vdma[i] = r * C::RB + 16 * (pc ^ row_swz<D>(r));  // V: row reads
+  }
+
+  // Q and dO fragments (B operands): step s, half g holds dims [16s + 8g, +8) of query qi.
+  u32x4 qf[C::QS], dof[C::QS];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) {
+    const bool ok = qi < p.Sq;
+    qf[s] = ok ? *(const u32x4*)((const unsigned char*)p.q + (qo_row0 + qi) * C::RB + 32 * s + 16 * g)
+               : u32x4{0, 0, 0, 0};
+    dof[s] = ok ? *(const u32x4*)((const unsigned char*)p.dout + (qo_row0 + qi) * C::RB + 32 * s + 16 * g)
+                : u32x4{0, 0, 0, 0};
+  }
+  // Padding rows (qi >= Sq) have Q = dO = 0, lse = delta = 0: every dS there is 0.
+  const float lse2 = qi < p.Sq ? p.lse[qo_row0 + qi] * kLog2e : 0.f;
+  const float dlt = qi < p.Sq ? p.delta[qo_row0 + qi] : 0.f;
+
+  int k_rd[C::QS], v_rd[C::QS], kt_rd[C::DB];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) {
+    k_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ tr_swz<D>(i32));
+    v_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ row_swz<D>(i32));
+  }
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) kt_rd[db] = tr_offset<D>(lane, db);
+
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  const float c = p.qk_scale_log2;
+
+  auto compute_tile = [&](int kt, const unsigned char* kl, const unsigned char* vl) {
+    const int kv0 = kt * C::BT;
+    u32x4 dsf[4];  // dS^T operand: chunk kc, element e <-> key 16kc + 8(e/4) + 4g + e%4
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st) {
+        const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[st]),
+                                                    s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st) {
+        const u32x4 a = *(const u32x4*)(vl + kb * 32 * C::RB + v_rd[st]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, dof[st]), dp, 0, 0, 0);
+      }
+      // register r on half g: key kv0 + 32kb + 8(r/4) + 4g + r%4
+      const int kb0 = kv0 + 32 * kb;
+      const bool edge = (CAUSAL && kb0 + 31 > qw + p.causal_off) || kb0 + 32 > p.Sk;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
+        if (edge) {
+          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key < p.Sk && (!CAUSAL || key <= qi + p.causal_off);
+          pr = ok ? pr : 0.f;
+        }
+        ds[r] = pr * (dp[r] - dlt);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) dsf[2 * kb + j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kl + 16 * kc * C::RB + kt_rd[db], C::RB),
+                                                          __builtin_bit_cast(bf16x8, dsf[kc]), acc[db], 0, 0, 0);
+  };
+
+  const int kv_bytes = p.Sk * C::RB;
+  unsigned char* const kd0 = k_lds0 + 1024 * C::DMA * wave;
+  unsigned char* const vd0 = v_lds0 + 1024 * C::DMA * wave;
+  unsigned char* const kd1 = k_lds1 + 1024 * C::DMA * wave;
+  unsigned char* const vd1 = v_lds1 + 1024 * C::DMA * wave;
+  if (n_tiles > 0) {
+    dma_tile<C::DMA>(kbase, C::TILE, 0, kv_bytes, kdma, kd0);
+    dma_tile<C::DMA>(vbase, C::TILE, 0, kv_bytes, vdma, vd0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < n_tiles; kt += 2) {
+    if (kt + 1 < n_tiles) {
+      dma_tile<C::DMA>(kbase, C::TILE, kt + 1, kv_bytes, kdma, kd1);
+      dma_tile<C::DMA>(vbase, C::TILE, kt + 1, kv_bytes, vdma, vd1);
+    }
+    if (kt < wave_tiles) compute_tile(kt, k_lds0, v_lds0);
+    __syncthreads();
+    if (kt + 1 >= n_tiles) break;
+    if (kt + 2 < n_tiles) {
+      dma_tile<C::DMA>(kbase, C::TILE, kt + 2, kv_bytes, kdma, kd0);
+      dma_tile<C::DMA>(vbase, C::TILE, kt + 2, kv_bytes, vdma, vd0);
+    }
+    if (kt + 1 < wave_tiles) compute_tile(kt + 1, k_lds1, v_lds1);
+    __syncthreads();
+  }
+
+  if (!wave_active || qi >= p.Sq) return;
+  unsigned char* row = (unsigned char*)p.dq + (qo_row0 + qi) * C::RB;
+  const float sc = p.scale;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;  // registers 4q4..4q4+3 hold dims d..d+3
+      *(u32x2*)(row + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * sc, acc[db][4 * q4 + 1] * sc),
+                                     pack_bf16x2(acc[db][4 * q4 + 2] * sc, acc[db][4 * q4 + 3] * sc)};
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1)))
+void attn_bwd_dkdv_kernel(const BwdParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[C::TILE];  // dO
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int i32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int BH = p.B * p.Hkv;
+  const int kt = blockIdx.x / BH;  // ascending: under the mask the first keys see the most queries
+  const int rem = blockIdx.x - kt * BH;
+  const int b = rem / p.Hkv;
+  const int hk = rem - b * p.Hkv;
+
+  const int k0 = kt * 128;
+  const int kw = k0 + 32 * wave;
+  const int kj = kw + i32;  // this lane's key
+  const bool wave_active = kw < p.Sk;
+  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
+
+  // K and V rows of this lane's key (B operands): step s, half g holds dims [16s + 8g, +8).
+  u32x4 kf[C::QS], vf[C::QS];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) {
+    const bool ok = kj < p.Sk;
+    kf[s] = ok ? *(const u32x4*)((const unsigned char*)p.k + (kv_row0 + kj) * C::RB + 32 * s + 16 * g)
+               : u32x4{0, 0, 0, 0};
+    vf[s] = ok ? *(const u32x4*)((const unsigned char*)p.v + (kv_row0 + kj) * C::RB + 32 * s + 16 * g)
+               : u32x4{0, 0, 0, 0};
+  }
+
+  unsigned qdma[C::DMA];
+#pragma unroll
+  for (int i = 0; i < C::DMA; ++i) {
+    const int r = (64 * (C::DMA * wave + i) + lane) / C::CH;
+    qdma[i] = r * C::RB + 16 * ((lane % C::CH) ^ tr_swz<D>(r));  // Q and dO: row and transposing reads
+  }
+  int q_rd[C::QS], t_rd[C::DB];
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) q_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ tr_swz<D>(i32));
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) t_rd[db] = tr_offset<D>(lane, db);
+
+  f32x16 dk[C::DB], dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  const float c = p.qk_scale_log2;
+  const int off = p.causal_off;
+  // Queries that see a key of this workgroup: i >= k0 - off (all of them without the mask).
+  const int t_first = CAUSAL ? max(0, k0 - off) / C::BT : 0;
+  const int n_qt = (p.Sq + C::BT - 1) / C::BT;
+
+  size_t qo_row0 = 0;
+  auto compute_tile = [&](int t, const unsigned char* ql, const unsigned char* ol) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = t * C::BT + 32 * qb;
+      if (qb0 >= p.Sq) continue;
+      if (CAUSAL && qb0 + 31 + off < kw) continue;  // no query of the block sees a key of this wave
+      // S = Q K^T, dP = dO V^T: lane = key kj, register r on half g <-> query qb0 + 8(r/4) + 4g + r%4
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st) {
+        const u32x4 a = *(const u32x4*)(ql + 32 * qb * C::RB + q_rd[st]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, kf[st]),
+                                                    s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st) {
+        const u32x4 a = *(const u32x4*)(ol + 32 * qb * C::RB + q_rd[st]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, vf[st]), dp, 0, 0, 0);
+      }
+      const bool edge = (CAUSAL && kw + 31 > qb0 + off) || qb0 + 32 > p.Sq || kw + 32 > p.Sk;
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qq = qb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool valid = qq < p.Sq;
+        const float l2 = valid ? p.lse[qo_row0 + qq] * kLog2e : 0.f;
+        const float dl = valid ? p.delta[qo_row0 + qq] : 0.f;
+        float x = exp2_fast(__builtin_fmaf(s[r], c, -l2));
+        if (edge) {
+          const bool ok = valid && kj < p.Sk && (!CAUSAL || kj <= qq + off);
+          x = ok ? x : 0.f;
+        }
+        pr[r] = x;
+        ds[r] = x * (dp[r] - dl);
+      }
+      // P and dS operands: chunk kc, element e <-> query qb0 + 16kc + 8(e/4) + 4g + e%4
+      u32x4 pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          pf[j][e2] = pack_bf16x2(pr[8 * j + 2 * e2], pr[8 * j + 2 * e2 + 1]);
+          dsf[j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
+        }
+      // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const int base = (32 * qb + 16 * kc) * C::RB + t_rd[db];
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ol + base, C::RB),
+                                                           __builtin_bit_cast(bf16x8, pf[kc]), dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ql + base, C::RB),
+                                                           __builtin_bit_cast(bf16x8, dsf[kc]), dk[db], 0, 0, 0);
+        }
+    }
+  };
+
+  const int q_bytes = p.Sq * C::RB;
+  unsigned char* const qd0 = q_lds0 + 1024 * C::DMA * wave;
+  unsigned char* const od0 = o_lds0 + 1024 * C::DMA * wave;
+  unsigned char* const qd1 = q_lds1 + 1024 * C::DMA * wave;
+  unsigned char* const od1 = o_lds1 + 1024 * C::DMA * wave;
+  for (int gq = 0; gq < p.group; ++gq) {
+    const int hq = hk * p.group + gq;
+    qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+    const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
+    const unsigned char* obase = (const unsigned char*)p.dout + qo_row0 * C::RB;
+    if (t_first < n_qt) {
+      dma_tile<C::DMA>(qbase, C::TILE, t_first, q_bytes, qdma, qd0);
+      dma_tile<C::DMA>(obase, C::TILE, t_first, q_bytes, qdma, od0);
+    }
+    __syncthreads();
+    for (int t = t_first; t < n_qt; t += 2) {
+      if (t + 1 < n_qt) {
+        dma_tile<C::DMA>(qbase, C::TILE, t + 1, q_bytes, qdma, qd1);
+        dma_tile<C::DMA>(obase, C::TILE, t + 1, q_bytes, qdma, od1);
+      }
+      if (wave_active) compute_tile(t, q_lds0, o_lds0);
+      __syncthreads();
+      if (t + 1 >= n_qt) break;
+      if (t + 2 < n_qt) {
+        dma_tile<C::DMA>(qbase, C::TILE, t + 2, q_bytes, qdma, qd0);
+        dma_tile<C::DMA>(obase, C::TILE, t + 2, q_bytes, qdma, od0);
+      }
+      if (wave_active) compute_tile(t + 1, q_lds1, o_lds1);
+      __syncthreads();
+    }
+  }
+
+  if (!wave_active || kj >= p.Sk) return;
+  unsigned char* krow = (unsigned char*)p.dk + (kv_row0 + kj) * C::RB;
+  unsigned char* vrow = (unsigned char*)p.dv + (kv_row0 + kj) * C::RB;
+  const float sc = p.scale;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * g;
+      *(u32x2*)(krow + 2 * d) = u32x2{pack_bf16x2(dk[db][4 * q4] * sc, dk[db][4 * q4 + 1] * sc),
+                                      pack_bf16x2(dk[db][4 * q4 + 2] * sc, dk[db][4 * q4 + 3] * sc)};
+      *(u32x2*)(vrow + 2 * d) = u32x2{pack_bf16x2(dv[db][4 * q4], dv[db][4 * q4 + 1]),
+                                      pack_bf16x2(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3])};
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_d(const BwdParams& bp, hipStream_t stream) {
+  BwdParams arg = bp;
+  void* args[] = {&arg};
+  const size_t rows = (size_t)bp.B * bp.Hq * bp.Sq;
+  constexpr int RPB = 256 / (D / 8);
+  hipError_t e = hipLaunchKernel((const void*)&attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
+                                 dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel((const void*)&attn_bwd_dq_kernel<D, CAUSAL>,
+                      dim3((unsigned)bp.n_qtiles * (unsigned)bp.B * (unsigned)bp.Hq), dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&attn_bwd_dkdv_kernel<D, CAUSAL>,
+                         dim3((unsigned)bp.n_ktiles * (unsigned)bp.B * (unsigned)bp.Hkv), dim3(256), args, 0, stream);
+}
+
+}  // namespace bwd
+
+hipError_t launch_attn_bwd_bf16(const BwdParams& bp, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? bwd::launch_d<128, true>(bp, stream) : bwd::launch_d<128, false>(bp, stream);
+  return causal ? bwd::launch_d<64, true>(bp, stream) : bwd::launch_d<64, false>(bp, stream);
+}
+
+}  // namespace sdpa18

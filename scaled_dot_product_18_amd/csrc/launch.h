@@ -47,4 +47,30 @@ struct SplitParams {
 // merges the chunks into o and lse.
 hipError_t launch_attn_splitkv_bf16(const SplitParams& sp, int d, bool causal, hipStream_t stream);
 
+// Backward pass (attn_bwd.hip). q/o/dout/dq are [B,Hq,Sq,D], k/v/dk/dv
+// [B,Hkv,Sk,D], lse and delta [B,Hq,Sq]; all dense row-major, bf16 except
+// lse / delta (fp32).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // forward log-sum-exp, natural log
+  float* delta;      // workspace: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Sq, Sk;
+  int group;            // Hq / Hkv
+  int causal_off;       // Sk - Sq under the causal mask, else 0
+  float scale;          // multiplier of the dot products
+  float qk_scale_log2;  // scale * log2(e)
+  int n_qtiles;         // ceil(Sq / 128): dQ workgroups per (batch, query head)
+  int n_ktiles;         // ceil(Sk / 128): dK/dV workgroups per (batch, KV head)
+};
+
+// bf16, d in {64, 128}: delta, then dQ, then dK and dV, on one stream.
+hipError_t launch_attn_bwd_bf16(const BwdParams& bp, int d, bool causal, hipStream_t stream);
+
 }  // namespace sdpa18

@@ -130,6 +130,14 @@ def quantise_e4m3(x: torch.Tensor):
     return codes.contiguous(), descale
 
 
+def draw_grad(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """A seeded upstream gradient dL/dO for the backward pass: N(0,1) of O's
+    shape [B, Hq, Sq, d], rounded to bf16 (its own stream of the workload's seed)."""
+    seed = w.seed if seed is None else seed
+    g = _normal(np.random.SeedSequence([seed, 3]), (w.B, w.Hq, w.Sq, w.d))
+    return torch.from_numpy(g).to(torch.bfloat16)
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     """Inputs for workload ``w`` as torch CPU tensors in the storage dtype.
 

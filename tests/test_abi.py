@@ -32,8 +32,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _header_functions() == ["attn_fwd", "attn_fwd_fp8", "attn_fwd_splitkv", "attn_fwd_splitkv_plan",
-                                   "attn_strerror", "attn_version"]
+    assert _header_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp8",
+                                   "attn_fwd_splitkv", "attn_fwd_splitkv_plan", "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -149,6 +149,34 @@ def test_splitkv_plan(lib, sizes, ns):
     if ns == 0:
         items = B * Hkv * -(-(Hq // Hkv) * Sq // 32)
         assert items * n >= 256 or n == min(128, -(-Sk // 256)) or n == -(-Sk // 32)
+
+
+def test_bwd_validation_errors(lib):
+    f = lib.load().attn_bwd
+    ok = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
+              causal=1, dtype=1, ws=P, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                 a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"],
+                 None)
+
+    assert call(dtype=0) == -6 and call(dtype=2) == -6
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call(**{name: None}) == -1, name
+    assert call(Sk=0) == -2
+    assert call(Hkv=3) == -3
+    assert call(d=32) == -4
+    assert call(Sq=9) == -5
+    assert call(scale=float("nan")) == -7
+    assert call(dk=P + 2) == -8 and call(do=P + 8) == -8
+    assert call(ws=None) == -10 and call(ws=P + 4) == -10
+    st, nbytes = lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 128)
+    assert st == 0 and nbytes == 4 * 8 * 4
+    assert call(ws_bytes=nbytes - 1) == -10
+    assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 128)[0] == -3
+    assert lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 96)[0] == -4
 
 
 def test_python_wrapper_rejects_cpu_tensors():
