@@ -177,9 +177,10 @@ int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num
  *             query heads, computed without atomics);
  *   dtype     ATTN_BF16 only: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse;
  *   workspace device memory owned by the caller, 16-byte aligned, at least
- *             attn_bwd_workspace_size bytes (B*Hq*Sq floats: the per-row
- *             rowsum(dout * O)); contents on entry ignored, unspecified on
- *             return; two calls in flight need two workspaces.
+ *             attn_bwd_workspace_size bytes (2*B*Hq*Sq floats: the per-row
+ *             rowsum(dout * O), then lse * log2(e)); contents on entry
+ *             ignored, unspecified on return; two calls in flight need two
+ *             workspaces.
  *   Other arguments as attn_fwd.
  *
  * Returns ATTN_OK or a negative status: ATTN_ERR_NULL if any of q, k, v, o,

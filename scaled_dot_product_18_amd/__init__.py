@@ -157,7 +157,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     ``want_lse=True`` and the same ``causal`` and ``scale``; ``dout`` is the
     gradient of the loss with respect to ``o``. dk and dv have k's shape (with
     GQA/MQA they sum over the query heads that share a KV head). ``workspace``
-    (B*Hq*Sq float32) is allocated here when not given.
+    (2*B*Hq*Sq float32) is allocated here when not given.
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t.dtype != torch.bfloat16:

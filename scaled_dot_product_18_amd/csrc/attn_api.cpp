@@ -185,7 +185,7 @@ int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  if (workspace_bytes != nullptr) *workspace_bytes = (size_t)B * Hq * Sq * sizeof(float);
+  if (workspace_bytes != nullptr) *workspace_bytes = 2 * (size_t)B * Hq * Sq * sizeof(float);
   return ATTN_OK;
 }
 
@@ -200,7 +200,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if ((int64_t)((Sk + 127) / 128) * B * Hkv >= INT32_MAX) return ATTN_ERR_SHAPE;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
   if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
-  const size_t need = (size_t)B * Hq * Sq * sizeof(float);
+  const size_t rows = (size_t)B * Hq * Sq;
+  const size_t need = 2 * rows * sizeof(float);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   sdpa18::BwdParams bp;
   bp.q = q;
@@ -210,6 +211,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.dout = dout;
   bp.lse = lse;
   bp.delta = static_cast<float*>(workspace);
+  bp.lse2 = static_cast<float*>(workspace) + rows;
   bp.dq = dq;
   bp.dk = dk;
   bp.dv = dv;

@@ -32,6 +32,7 @@ namespace sdpa18 {
 namespace bwd {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -89,6 +90,14 @@ __device__ __forceinline__ int tr_offset(int lane, int db) {
   return r * (2 * D) + 16 * ((d >> 3) ^ tr_swz<D>(r)) + 2 * (d & 7);
 }
 
+// 64 consecutive fp32 per-row statistics of tile t (one per query of the tile)
+// HBM -> LDS, lane l filling dst + 4 l; rows past the end load as zeros.
+__device__ __forceinline__ void dma_stat(const float* base, int t, int total_bytes, int lane, unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + 64 * t), (short)0, total_bytes - 256 * t, kBufferConfig);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, 4 * lane, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* p, int rb) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * rb));
@@ -99,7 +108,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------- delta
-// delta[row] = sum_c dO[row, c] * O[row, c]; D/8 lanes per row, 8 elements each.
+// delta[row] = sum_c dO[row, c] * O[row, c] and lse2[row] = lse[row] * log2(e);
+// D/8 lanes per row, 8 elements each.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_bwd_delta_kernel(const BwdParams p) {
@@ -117,7 +127,10 @@ void attn_bwd_delta_kernel(const BwdParams p) {
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (row < rows && part == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -290,6 +303,9 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[C::TILE];  // dO
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[C::TILE];
+  // lse2 and delta of the tile's 64 queries, streamed with the tile
+  __shared__ __attribute__((aligned(256))) float st_lds0[2 * C::BT];
+  __shared__ __attribute__((aligned(256))) float st_lds1[2 * C::BT];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -345,7 +361,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   const int n_qt = (p.Sq + C::BT - 1) / C::BT;
 
   size_t qo_row0 = 0;
-  auto compute_tile = [&](int t, const unsigned char* ql, const unsigned char* ol) {
+  auto compute_tile = [&](int t, const unsigned char* ql, const unsigned char* ol, const float* stl) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int qb0 = t * C::BT + 32 * qb;
@@ -366,16 +382,22 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
                                                      __builtin_bit_cast(bf16x8, vf[st]), dp, 0, 0, 0);
       }
       const bool edge = (CAUSAL && kw + 31 > qb0 + off) || qb0 + 32 > p.Sq || kw + 32 > p.Sk;
+      // lse2 / delta of queries qb0 + 8m + 4g + (0..3): one 16-byte LDS read each
+      f32x4 l2v[4], dlv[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        l2v[m] = *(const f32x4*)(stl + 32 * qb + 8 * m + 4 * g);
+        dlv[m] = *(const f32x4*)(stl + C::BT + 32 * qb + 8 * m + 4 * g);
+      }
       float pr[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qq = qb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool valid = qq < p.Sq;
-        const float l2 = valid ? p.lse[qo_row0 + qq] * kLog2e : 0.f;
-        const float dl = valid ? p.delta[qo_row0 + qq] : 0.f;
+        const float l2 = l2v[r >> 2][r & 3];
+        const float dl = dlv[r >> 2][r & 3];
         float x = exp2_fast(__builtin_fmaf(s[r], c, -l2));
         if (edge) {
-          const bool ok = valid && kj < p.Sk && (!CAUSAL || kj <= qq + off);
+          const bool ok = qq < p.Sq && kj < p.Sk && (!CAUSAL || kj <= qq + off);
           x = ok ? x : 0.f;
         }
         pr[r] = x;
@@ -414,24 +436,31 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
     const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
     const unsigned char* obase = (const unsigned char*)p.dout + qo_row0 * C::RB;
+    // wave 0 streams lse2, wave 1 delta: 64 floats per tile, one 4-byte DMA per lane
+    const float* stat = (wave == 0 ? p.lse2 : p.delta) + qo_row0;
+    const int st_bytes = p.Sq * 4;
+    const int st_dst = wave == 0 ? 0 : 4 * C::BT;
     if (t_first < n_qt) {
       dma_tile<C::DMA>(qbase, C::TILE, t_first, q_bytes, qdma, qd0);
       dma_tile<C::DMA>(obase, C::TILE, t_first, q_bytes, qdma, od0);
+      if (wave < 2) dma_stat(stat, t_first, st_bytes, lane, (unsigned char*)st_lds0 + st_dst);
     }
     __syncthreads();
     for (int t = t_first; t < n_qt; t += 2) {
       if (t + 1 < n_qt) {
         dma_tile<C::DMA>(qbase, C::TILE, t + 1, q_bytes, qdma, qd1);
         dma_tile<C::DMA>(obase, C::TILE, t + 1, q_bytes, qdma, od1);
+        if (wave < 2) dma_stat(stat, t + 1, st_bytes, lane, (unsigned char*)st_lds1 + st_dst);
       }
-      if (wave_active) compute_tile(t, q_lds0, o_lds0);
+      if (wave_active) compute_tile(t, q_lds0, o_lds0, st_lds0);
       __syncthreads();
       if (t + 1 >= n_qt) break;
       if (t + 2 < n_qt) {
         dma_tile<C::DMA>(qbase, C::TILE, t + 2, q_bytes, qdma, qd0);
         dma_tile<C::DMA>(obase, C::TILE, t + 2, q_bytes, qdma, od0);
+        if (wave < 2) dma_stat(stat, t + 2, st_bytes, lane, (unsigned char*)st_lds0 + st_dst);
       }
-      if (wave_active) compute_tile(t + 1, q_lds1, o_lds1);
+      if (wave_active) compute_tile(t + 1, q_lds1, o_lds1, st_lds1);
       __syncthreads();
     }
   }

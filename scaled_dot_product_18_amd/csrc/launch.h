@@ -48,8 +48,8 @@ struct SplitParams {
 hipError_t launch_attn_splitkv_bf16(const SplitParams& sp, int d, bool causal, hipStream_t stream);
 
 // Backward pass (attn_bwd.hip). q/o/dout/dq are [B,Hq,Sq,D], k/v/dk/dv
-// [B,Hkv,Sk,D], lse and delta [B,Hq,Sq]; all dense row-major, bf16 except
-// lse / delta (fp32).
+// [B,Hkv,Sk,D], lse, delta and lse2 [B,Hq,Sq]; all dense row-major, bf16
+// except lse / delta / lse2 (fp32).
 struct BwdParams {
   const void* q;
   const void* k;
@@ -58,6 +58,7 @@ struct BwdParams {
   const void* dout;
   const float* lse;  // forward log-sum-exp, natural log
   float* delta;      // workspace: rowsum(dO * O)
+  float* lse2;       // workspace: lse * log2(e)
   void* dq;
   void* dk;
   void* dv;

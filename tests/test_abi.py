@@ -173,7 +173,7 @@ def test_bwd_validation_errors(lib):
     assert call(dk=P + 2) == -8 and call(do=P + 8) == -8
     assert call(ws=None) == -10 and call(ws=P + 4) == -10
     st, nbytes = lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 128)
-    assert st == 0 and nbytes == 4 * 8 * 4
+    assert st == 0 and nbytes == 2 * 4 * 8 * 4
     assert call(ws_bytes=nbytes - 1) == -10
     assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 128)[0] == -3
     assert lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 96)[0] == -4
