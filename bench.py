@@ -16,7 +16,9 @@ with cuDNN and TransformerEngine", section 8: warm-up calls first, inputs
 already on the device, warm caches), with device events instead of host time.
 
 --workload takes any name of sdpa_inputs.WORKLOADS. The decode workload runs
-the split-KV path (one step = the chunk kernel plus the merge kernel); a
+the split-KV path (one step = the chunk kernel plus the merge kernel), the
+backward workload one attn_bwd call (delta, dQ and dK/dV kernels; its FLOP are
+the five products of the backward pass, 2.5 times the forward's); a
 workload whose arithmetic intensity is below the ridge point reports the HBM
 roofline (algorithmic bytes per launch over the launch time) instead of the
 matrix-core one.
@@ -42,6 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (causal-adjusted) and % of MFMA peak, 1 MI355X"
+METRIC_BWD = "attention bwd TFLOP/s (causal-adjusted, five products) and % of MFMA peak, 1 MI355X"
 
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
@@ -58,7 +61,7 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
                   "attn_fwd_fp8_pp_kernel": "attn_fwd_fp8_pp.hip",
                   "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip",
-                  "attn_fwd_splitkv_kernel": "attn_fwd_splitkv.hip"}
+                  "attn_fwd_splitkv_kernel": "attn_fwd_splitkv.hip", "attn_bwd_dkdv_kernel": "attn_bwd.hip"}
 SHARED_SOURCES = ("kernel_common.h", "launch.h", "attn_api.cpp")
 
 
@@ -77,6 +80,8 @@ def kernel_source_hash(kernel: str) -> str:
 def kernel_name(w) -> str:
     if w.path == "splitkv":
         return "attn_fwd_splitkv_kernel"
+    if w.path == "bwd":
+        return "attn_bwd_dkdv_kernel"
     if w.dtype == "bf16" and w.d == 128:
         return "attn_fwd_bf16_pp_kernel"
     if w.dtype == "fp8" and w.d == 128:
@@ -134,7 +139,11 @@ def cpu_baseline(w, inp, budget_s: float = 15.0) -> dict:
             q = as64(inp["q"][b, h], "q")[None, None]
             k = as64(inp["k"][b, h // G], "k")[None, None]
             v = as64(inp["v"][b, h // G], "v")[None, None]
-            oracle.attention(q, k, v, w.scale, w.causal)
+            if w.path == "bwd":
+                oracle.attention_backward(q, k, v, inp["dout"][b, h].to(torch.float64).numpy()[None, None],
+                                          w.scale, w.causal)
+            else:
+                oracle.attention(q, k, v, w.scale, w.causal)
             heads += 1
             elapsed = time.perf_counter() - t0
             if elapsed >= budget_s:
@@ -268,9 +277,19 @@ def main() -> int:
     if w.path == "splitkv":
         _, nbytes = sdpa.splitkv_plan(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    if w.path == "bwd":
+        # The backward step's inputs: the forward's O and lse (computed here, before timing) and a seeded dO.
+        inp["dout"] = sdpa_inputs.draw_grad(w)
+        dev["dout"] = inp["dout"].cuda()
+        dev["o"], dev["lse"] = sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
+                                        want_lse=True)
+        workspace = torch.empty(2 * w.B * w.Hq * w.Sq * 4, dtype=torch.uint8, device="cuda")
 
     def step():
-        if w.path == "splitkv":
+        if w.path == "bwd":
+            sdpa.bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["lse"], dev["dout"], causal=w.causal, scale=w.scale,
+                     workspace=workspace)
+        elif w.path == "splitkv":
             sdpa.fwd_splitkv(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, out=out, lse_out=lse,
                              workspace=workspace)
         elif w.dtype == "fp8":
@@ -322,7 +341,7 @@ def main() -> int:
     else:
         bound, unit_r, peak_r, achieved_r = "mfma", "TFLOP/s", peak, achieved
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if w.path == "bwd" else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -333,7 +352,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: seeded i.i.d. N(0,1) q/k/v" + (", per-tensor amax e4m3fn" if w.dtype == "fp8" else ""),
+        "data": "synthetic: seeded i.i.d. N(0,1) q/k/v" + (", per-tensor amax e4m3fn" if w.dtype == "fp8" else "")
+                + (", N(0,1) dO; O and lse from the forward kernel" if w.path == "bwd" else ""),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
                    "causal": w.causal, "lse": w.want_lse, "in_dtype": w.dtype, "path": w.path,
                    "out_dtype": "f32" if w.dtype == "f32" else "bf16", "parallelism": "single GPU"},

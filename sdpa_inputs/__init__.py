@@ -10,9 +10,9 @@ Workloads follow the pages' shapes:
     64 -- "Self-attention, CUDA kernels and FlashAttention", section 1;
     causal bf16 MHA; causal GQA/MQA with shared KV heads -- codelab
     "Accelerate attention on GPU with cuDNN and TransformerEngine", section 9;
-    and a long causal fp8-e4m3 workload -- same codelab, section 10); the
-    last is a decode step (one query per sequence against a long KV cache,
-    GQA heads of section 9) for the split-KV path;
+    and a long causal fp8-e4m3 workload -- same codelab, section 10); then a
+    decode step (one query per sequence against a long KV cache, GQA heads of
+    section 9) for the split-KV path, and the causal GQA shape's backward pass;
   * every draw is i.i.d. standard normal, as every input cell of the codelab
     is (sections 3, 8, 9, 10), and bf16 values are fp32 draws cast to bf16
     (section 6).
@@ -53,15 +53,19 @@ class Workload:
     causal: bool
     seed: int
     want_lse: bool = False
-    path: str = "fused"  # "fused": attn_fwd / attn_fwd_fp8; "splitkv": attn_fwd_splitkv (decode shapes)
+    path: str = "fused"  # "fused": attn_fwd / attn_fwd_fp8; "splitkv": attn_fwd_splitkv; "bwd": attn_bwd
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     def flops(self) -> float:
-        """Causal-adjusted algorithmic FLOP: 4*B*Hq*Sq*Sk*d, halved when causal."""
+        """Causal-adjusted algorithmic FLOP: 4*B*Hq*Sq*Sk*d, halved when causal (two
+        Sq x Sk x d products). The backward pass has five such products (S, dP, dV,
+        dK, dQ; recomputation not counted): 2.5 times the forward."""
         f = 4.0 * self.B * self.Hq * self.Sq * self.Sk * self.d
+        if self.path == "bwd":
+            f *= 2.5
         return f * 0.5 if self.causal else f
 
     def hbm_bytes(self) -> float:
@@ -72,6 +76,9 @@ class Workload:
         kv = 2 * self.B * self.Hkv * self.Sk * self.d * ein
         o = self.B * self.Hq * self.Sq * self.d * eout
         lse = self.B * self.Hq * self.Sq * 4 if self.want_lse else 0
+        if self.path == "bwd":
+            # reads Q, K, V, O, dO and lse once; writes dQ, dK, dV once
+            return float(2 * q + 2 * kv + 2 * o + self.B * self.Hq * self.Sq * 4)
         return float(q + kv + o + lse)
 
 
@@ -88,6 +95,9 @@ WORKLOADS: Dict[str, Workload] = {
         # One new token per sequence against a 32K-token KV cache, the GQA cell's head layout.
         Workload("decode_gqa_bf16_b4_hq32_hkv8_sk32768_d128", 4, 32, 8, 1, 32768, 128, "bf16", False, 42,
                  path="splitkv"),
+        # The headline shape's backward pass (dQ, dK, dV from the forward's O and lse and a seeded dO).
+        Workload("bwd_causal_gqa_bf16_b4_hq32_hkv8_s4096_d128", 4, 32, 8, 4096, 4096, 128, "bf16", True, 42,
+                 path="bwd"),
     ]
 }
 

@@ -91,3 +91,32 @@ def test_bwd_errors_raise_through_python(gpu):
     with pytest.raises(sdpa.AttnError) as e:
         sdpa.bwd(z, z, z, z, lse, z, workspace=torch.empty(8, dtype=torch.uint8, device="cuda"))
     assert e.value.status == -10
+
+
+def test_bwd_benchmark_workload_sampled_groups(gpu):
+    """The benchmark's backward workload (causal GQA B4 Hq32 Hkv8 S4096 d128), launched as the
+    benchmark launches it; two whole KV-head groups (their 4 query heads' dQ and the KV head's dK,
+    dV: every element) are compared with the oracle run on that group alone."""
+    import scaled_dot_product_18_amd as sdpa
+    w = sdpa_inputs.WORKLOADS["bwd_causal_gqa_bf16_b4_hq32_hkv8_s4096_d128"]
+    assert w.path == "bwd"
+    log(f"[bwd-full] {w.name}")
+    inp = sdpa_inputs.make_inputs(w)
+    g = sdpa_inputs.draw_grad(w)
+    q, k, v, do = (t.cuda() for t in (inp["q"], inp["k"], inp["v"], g))
+    o, lse = sdpa.fwd(q, k, v, causal=True, scale=w.scale, want_lse=True)
+    dq, dk, dv = sdpa.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hk in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        hs = slice(hk * G, (hk + 1) * G)
+        ref = attention_backward(inp["q"][b:b + 1, hs].double().numpy(), inp["k"][b:b + 1, hk:hk + 1].double().numpy(),
+                                 inp["v"][b:b + 1, hk:hk + 1].double().numpy(), g[b:b + 1, hs].double().numpy(),
+                                 w.scale, True)
+        for name, got, r in zip(("dq", "dk", "dv"), (dq[b:b + 1, hs], dk[b:b + 1, hk:hk + 1], dv[b:b + 1, hk:hk + 1]),
+                                ref):
+            x = got.double().cpu().numpy()
+            err = float(np.abs(x - r).max())
+            scale = max(1.0, float(np.abs(r).max()))
+            log(f"  b{b} hk{hk} {name}: max err {err:.5f} scale {scale:.3f}")
+            assert np.isfinite(x).all() and err <= TOL * scale
