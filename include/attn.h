@@ -19,7 +19,7 @@
  * score tiles live only on chip, so no Sq x Sk matrix is written to memory;
  * lse is the small per-row statistic that manner keeps for a backward pass.
  *
- * Layouts (all dense, row-major, no strides):
+ * Layouts (dense, row-major; attn_fwd_strided takes strided q, k, v, o):
  *   q, o  : [B, Hq,  Sq, d]
  *   k, v  : [B, Hkv, Sk, d]
  *   lse   : [B, Hq,  Sq] float32, natural-log units (may be NULL)
@@ -42,6 +42,7 @@
 #define SDPA18_ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -69,7 +70,8 @@ enum {
   ATTN_ERR_ALIGN = -8,         /* a base pointer is not 16-byte aligned                 */
   ATTN_ERR_LAUNCH = -9,        /* the HIP runtime rejected the kernel launch            */
   ATTN_ERR_WORKSPACE = -10,    /* split-KV workspace missing, misaligned or too small   */
-  ATTN_ERR_SPLITS = -11        /* num_splits outside [0, 128]                           */
+  ATTN_ERR_SPLITS = -11,       /* num_splits outside [0, 128]                           */
+  ATTN_ERR_STRIDE = -12        /* attn_fwd_strided: unusable strides (see there)        */
 };
 
 /*
@@ -110,6 +112,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                  float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/*
+ * attn_fwd_strided -- attn_fwd / attn_fwd_fp8 on strided tensors, so that the
+ * codelab's own (B, T, N, H) arrays ("Accelerate attention on GPU with cuDNN
+ * and TransformerEngine", sections 3 and 4: batch, sequence, heads, head
+ * dimension) are read and written in place, without a permute.
+ *
+ *   strides  12 element strides: {batch, head, position} of q, then k, v, o.
+ *            Element [b, h, i, c] of q sits at q + b*s[0] + h*s[1] + i*s[2] + c;
+ *            the d elements of one position are contiguous. The dense layout
+ *            of attn_fwd is {Hq*Sq*d, Sq*d, d} for q and o; the codelab's
+ *            (B, T, N, H) is {T*N*H, H, N*H}.
+ *            Every stride must be >= 0, the position stride >= d, each stride
+ *            in bytes a multiple of 16, and one head's rows must span less
+ *            than 2 GiB; otherwise ATTN_ERR_STRIDE. Distinct (b, h, i) of o
+ *            must not overlap (not checked).
+ *   dtype    as attn_fwd; for ATTN_FP8_E4M3 descale_q/k/v are the per-tensor
+ *            descales of attn_fwd_fp8, for the other dtypes they must be 1.
+ *   lse      dense [B, Hq, Sq] as in attn_fwd.
+ *   Other arguments and the return value as attn_fwd.
+ */
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, const int64_t* strides,
+                     float scale, int causal, int dtype,
+                     float descale_q, float descale_k, float descale_v, hipStream_t stream);
 
 /*
  * attn_fwd_splitkv -- the same operation as attn_fwd, computed for few

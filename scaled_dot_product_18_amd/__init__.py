@@ -5,8 +5,10 @@
 computes softmax(scale * Q K^T [+ causal mask]) V in one fused HIP kernel
 (codelab "Accelerate attention on GPU with cuDNN and TransformerEngine",
 intro and sections 4, 7, 9; article "Self-attention, CUDA kernels and
-FlashAttention", section 3). Tensors are [B, H, S, d] on the GPU; K and V may
-have fewer heads than Q (GQA/MQA, query head h reads KV head h // (Hq/Hkv)).
+FlashAttention", section 3). Tensors are [B, H, S, d] on the GPU, or the
+codelab's (B, T, N, H) with ``layout="bshd"``; any strides with contiguous
+head dimension are read in place. K and V may have fewer heads than Q
+(GQA/MQA, query head h reads KV head h // (Hq/Hkv)).
 
 This module only marshals arguments into the C ABI of libsdpa18.so
 (include/attn.h); PyTorch supplies device memory and the current stream.
@@ -48,17 +50,36 @@ def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     for t in (q, k, v):
         if not t.is_cuda:
             raise ValueError("inputs must be GPU tensors")
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous [B, H, S, d]")
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension of every input must be contiguous (stride 1)")
         if t.device != q.device:
             raise ValueError("inputs must be on one device")
     return B, Hq, Hkv, Sq, Sk, d
 
 
-def _outputs(q, B, Hq, Sq, d, out_dtype, want_lse, out, lse_out):
+def _dense_only(*ts) -> None:
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("this entry point takes contiguous [B, H, S, d] tensors")
+
+
+def _as_bhsd(layout: str, *ts):
+    """Views in the library's [B, H, S, d] order: "bshd" tensors (the codelab's (B, T, N, H)) are
+    transposed as views, never copied."""
+    if layout == "bhsd":
+        return ts
+    if layout == "bshd":
+        return tuple(t.transpose(1, 2) for t in ts)
+    raise ValueError(f"layout must be 'bhsd' or 'bshd', got {layout!r}")
+
+
+def _outputs(q, B, Hq, Sq, d, out_dtype, want_lse, out, lse_out, layout="bhsd"):
     if out is None:
-        out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
-    elif out.shape != (B, Hq, Sq, d) or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        if layout == "bshd":
+            out = torch.empty((B, Sq, Hq, d), dtype=out_dtype, device=q.device).transpose(1, 2)
+        else:
+            out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, Hq, Sq, d) or out.dtype != out_dtype or out.stride(-1) != 1 or out.device != q.device:
         raise ValueError("out has the wrong shape, dtype, layout or device")
     lse = None
     if want_lse or lse_out is not None:
@@ -68,44 +89,67 @@ def _outputs(q, B, Hq, Sq, d, out_dtype, want_lse, out, lse_out):
     return out, lse
 
 
+def _strides(*ts):
+    return [x for t in ts for x in (t.stride(0), t.stride(1), t.stride(2))]
+
+
+def _launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, descales):
+    """attn_fwd / attn_fwd_fp8 for dense tensors, attn_fwd_strided otherwise."""
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    lp = lse.data_ptr() if lse is not None else None
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        if dtype == ATTN_FP8_E4M3:
+            return _lib.attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, Hq, Hkv, Sq, Sk,
+                                     d, scale, causal, *descales, stream)
+        return _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, Hq, Hkv, Sq, Sk, d,
+                             scale, causal, dtype, stream)
+    return _lib.attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lp, B, Hq, Hkv, Sq, Sk, d,
+                                 _strides(q, k, v, out), scale, causal, dtype, *descales, stream)
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
-        want_lse: bool = False, out: Optional[torch.Tensor] = None,
-        lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        want_lse: bool = False, out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+        layout: str = "bhsd") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Fused attention forward for float32 or bfloat16 inputs.
 
-    scale defaults to 1/sqrt(d). Returns (o, lse) with o in the input dtype and
-    lse float32 [B, Hq, Sq] (natural log) or None. Enqueued on the current
-    stream; nothing waits.
+    scale defaults to 1/sqrt(d). ``layout="bhsd"`` takes [B, H, S, d] tensors;
+    ``layout="bshd"`` takes the codelab's (B, T, N, H) and returns o in that
+    layout. Strided views are read in place (the head dimension must be
+    contiguous). Returns (o, lse) with o in the input dtype and lse float32
+    [B, Hq, Sq] (natural log) or None. Enqueued on the current stream; nothing
+    waits.
     """
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError(f"fwd takes float32 or bfloat16 q/k/v of one dtype, got {q.dtype}/{k.dtype}/{v.dtype}")
+    q, k, v = _as_bhsd(layout, q, k, v)
+    if out is not None:
+        (out,) = _as_bhsd(layout, out)
     B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out, lse = _outputs(q, B, Hq, Sq, d, q.dtype, want_lse, out, lse_out)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    _lib.check(_lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr() if lse is not None else None,
-                             B, Hq, Hkv, Sq, Sk, d, scale, causal, _DTYPES[q.dtype], stream))
+    out, lse = _outputs(q, B, Hq, Sq, d, q.dtype, want_lse, out, lse_out, layout)
+    _lib.check(_launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, _DTYPES[q.dtype], (1.0, 1.0, 1.0)))
+    (out,) = _as_bhsd(layout, out)
     return out, lse
 
 
 def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: float, descale_k: float,
             descale_v: float, *, causal: bool = False, scale: Optional[float] = None, want_lse: bool = False,
-            out: Optional[torch.Tensor] = None,
-            lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+            layout: str = "bhsd") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Fused attention forward on fp8-e4m3fn codes (uint8 or float8_e4m3fn tensors)
     with per-tensor descales; bfloat16 output. Other arguments as :func:`fwd`."""
     ok = (torch.uint8, torch.float8_e4m3fn)
     if q8.dtype not in ok or k8.dtype not in ok or v8.dtype not in ok:
         raise ValueError("fwd_fp8 takes uint8 or float8_e4m3fn codes")
+    q8, k8, v8 = _as_bhsd(layout, q8, k8, v8)
+    if out is not None:
+        (out,) = _as_bhsd(layout, out)
     B, Hq, Hkv, Sq, Sk, d = _shapes(q8, k8, v8)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out, lse = _outputs(q8, B, Hq, Sq, d, torch.bfloat16, want_lse, out, lse_out)
-    stream = torch.cuda.current_stream(q8.device).cuda_stream
-    _lib.check(_lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
-                                 lse.data_ptr() if lse is not None else None,
-                                 B, Hq, Hkv, Sq, Sk, d, scale, causal,
-                                 float(descale_q), float(descale_k), float(descale_v), stream))
+    out, lse = _outputs(q8, B, Hq, Sq, d, torch.bfloat16, want_lse, out, lse_out, layout)
+    _lib.check(_launch(q8, k8, v8, out, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_FP8_E4M3,
+                       (float(descale_q), float(descale_k), float(descale_v))))
+    (out,) = _as_bhsd(layout, out)
     return out, lse
 
 
@@ -131,8 +175,10 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError(f"fwd_splitkv takes bfloat16 q/k/v, got {q.dtype}/{k.dtype}/{v.dtype}")
     B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
+    _dense_only(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, B, Hq, Sq, d, q.dtype, want_lse, out, lse_out)
+    _dense_only(out)
     _, nbytes = splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
@@ -163,6 +209,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         if t.dtype != torch.bfloat16:
             raise ValueError(f"bwd takes bfloat16 tensors, {name} is {t.dtype}")
     B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
+    _dense_only(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
         if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must be a contiguous tensor of q's shape on q's device")

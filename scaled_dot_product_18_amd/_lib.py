@@ -29,6 +29,7 @@ STATUS = {
     -9: "ATTN_ERR_LAUNCH",
     -10: "ATTN_ERR_WORKSPACE",
     -11: "ATTN_ERR_SPLITS",
+    -12: "ATTN_ERR_STRIDE",
 }
 
 _lock = threading.Lock()
@@ -67,6 +68,9 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd.restype = i
         lib.attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
         lib.attn_bwd_workspace_size.restype = i
+        lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int64), f, i,
+                                         i, f, f, f, vp]
+        lib.attn_fwd_strided.restype = i
         lib.attn_strerror.argtypes = [i]
         lib.attn_strerror.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -121,3 +125,11 @@ def attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d):
     nbytes = ctypes.c_size_t(0)
     st = load().attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d, ctypes.byref(nbytes))
     return st, nbytes.value
+
+
+def attn_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, strides, scale, causal, dtype, dq, dk, dv,
+                     stream) -> int:
+    """Raw call with integer pointers and 12 element strides; returns the status code."""
+    arr = (ctypes.c_int64 * 12)(*[int(x) for x in strides])
+    return load().attn_fwd_strided(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, arr, scale, int(causal), dtype, dq, dk, dv,
+                                   stream)

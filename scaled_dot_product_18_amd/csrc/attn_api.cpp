@@ -36,9 +36,54 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
   return ATTN_OK;
 }
 
+// Element strides of q, k, v, o: {batch, head, position} for each, 12 values.
+struct Strides {
+  int64_t v[12];
+};
+
+Strides dense_strides(int Hq, int Hkv, int Sq, int Sk, int d) {
+  const int64_t qo[3] = {(int64_t)Hq * Sq * d, (int64_t)Sq * d, d};
+  const int64_t kv[3] = {(int64_t)Hkv * Sk * d, (int64_t)Sk * d, d};
+  Strides s;
+  for (int i = 0; i < 3; ++i) {
+    s.v[i] = qo[i];
+    s.v[3 + i] = kv[i];
+    s.v[6 + i] = kv[i];
+    s.v[9 + i] = qo[i];
+  }
+  return s;
+}
+
+// Every row 16-byte aligned (given aligned bases), rows of one head disjoint,
+// and a head's rows within the kernels' 32-bit offsets.
+bool strides_ok(const Strides& st, int Sq, int Sk, int d, int in_bytes, int out_bytes) {
+  for (int t = 0; t < 4; ++t) {
+    const int es = t == 3 ? out_bytes : in_bytes;
+    const int S = (t == 0 || t == 3) ? Sq : Sk;
+    const int64_t sb = st.v[3 * t], sh = st.v[3 * t + 1], ss = st.v[3 * t + 2];
+    if (sb < 0 || sh < 0 || ss < d) return false;
+    if ((sb * es) % 16 != 0 || (sh * es) % 16 != 0 || (ss * es) % 16 != 0) return false;
+    if (((int64_t)S - 1) * ss * es + (int64_t)d * es >= INT32_MAX || 128 * ss * es >= INT32_MAX) return false;
+  }
+  return true;
+}
+
 sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                               int Hkv, int Sq, int Sk, int causal, float qk_scale, float o_scale, int block_m) {
+                               int Hkv, int Sq, int Sk, int causal, float qk_scale, float o_scale, int block_m,
+                               const Strides& st, int in_bytes, int out_bytes) {
   sdpa18::AttnParams p;
+  p.q_sb = st.v[0] * in_bytes;
+  p.q_sh = st.v[1] * in_bytes;
+  p.q_ss = (int)(st.v[2] * in_bytes);
+  p.k_sb = st.v[3] * in_bytes;
+  p.k_sh = st.v[4] * in_bytes;
+  p.k_ss = (int)(st.v[5] * in_bytes);
+  p.v_sb = st.v[6] * in_bytes;
+  p.v_sh = st.v[7] * in_bytes;
+  p.v_ss = (int)(st.v[8] * in_bytes);
+  p.o_sb = st.v[9] * out_bytes;
+  p.o_sh = st.v[10] * out_bytes;
+  p.o_ss = (int)(st.v[11] * out_bytes);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -109,43 +154,63 @@ SplitPlan plan_splits(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_spl
   return pl;
 }
 
+
+// Shared path of attn_fwd, attn_fwd_fp8 and attn_fwd_strided (descales are 1 unless dtype is fp8).
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
+               int Sk, int d, const Strides& st, float scale, int causal, int dtype, float descale_q,
+               float descale_k, float descale_v, hipStream_t stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  const int s = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (s != ATTN_OK) return s;
+  const int in_bytes = dtype == ATTN_F32 ? 4 : dtype == ATTN_BF16 ? 2 : 1;
+  const int out_bytes = dtype == ATTN_F32 ? 4 : 2;
+  if (!strides_ok(st, Sq, Sk, d, in_bytes, out_bytes)) return ATTN_ERR_STRIDE;
+  if (!positive_finite(scale) || !positive_finite(descale_q) || !positive_finite(descale_k) ||
+      !positive_finite(descale_v))
+    return ATTN_ERR_SCALE;
+  const float qk = scale * descale_q * descale_k;
+  if (!positive_finite(qk * kLog2e)) return ATTN_ERR_SCALE;
+  if (dtype == ATTN_F32) {
+    const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, qk, 1.0f,
+                                             sdpa18::f32_block_m(), st, in_bytes, out_bytes);
+    return launch_status(sdpa18::launch_attn_f32(p, d, causal != 0, stream));
+  }
+  if (dtype == ATTN_BF16) {
+    const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, qk, 1.0f,
+                                             sdpa18::bf16_block_m(d), st, in_bytes, out_bytes);
+    return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
+  }
+  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, qk, descale_v,
+                                           sdpa18::fp8_block_m(d), st, in_bytes, out_bytes);
+  return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
+}
+
 }  // namespace
 
 extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
              int Sk, int d, float scale, int causal, int dtype, hipStream_t stream) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
-  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
-  if (st != ATTN_OK) return st;
-  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
-  if (dtype == ATTN_F32) {
-    const sdpa18::AttnParams p =
-        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::f32_block_m());
-    return launch_status(sdpa18::launch_attn_f32(p, d, causal != 0, stream));
-  }
-  if (dtype == ATTN_BF16) {
-    const sdpa18::AttnParams p =
-        make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::bf16_block_m(d));
-    return launch_status(sdpa18::launch_attn_bf16(p, d, causal != 0, stream));
-  }
-  const sdpa18::AttnParams p = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, sdpa18::fp8_block_m(d));
-  return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, dense_strides(Hq, Hkv, Sq, Sk, d), scale, causal, dtype,
+                    1.0f, 1.0f, 1.0f, stream);
 }
 
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int B, int Hq, int Hkv,
                  int Sq, int Sk, int d, float scale, int causal, float descale_q, float descale_k, float descale_v,
                  hipStream_t stream) {
-  const int st = validate(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, d, causal);
-  if (st != ATTN_OK) return st;
-  if (!positive_finite(scale) || !positive_finite(descale_q) || !positive_finite(descale_k) ||
-      !positive_finite(descale_v))
-    return ATTN_ERR_SCALE;
-  const float qk = scale * descale_q * descale_k;
-  if (!positive_finite(qk * kLog2e)) return ATTN_ERR_SCALE;
-  const sdpa18::AttnParams p =
-      make_params(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, causal, qk, descale_v, sdpa18::fp8_block_m(d));
-  return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
+  return fwd_common(q8, k8, v8, o_bf16, lse, B, Hq, Hkv, Sq, Sk, d, dense_strides(Hq, Hkv, Sq, Sk, d), scale, causal,
+                    ATTN_FP8_E4M3, descale_q, descale_k, descale_v, stream);
+}
+
+int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Sq, int Sk, int d, const int64_t* strides, float scale, int causal, int dtype,
+                     float descale_q, float descale_k, float descale_v, hipStream_t stream) {
+  if (strides == nullptr) return ATTN_ERR_NULL;
+  if (dtype != ATTN_FP8_E4M3 && (descale_q != 1.0f || descale_k != 1.0f || descale_v != 1.0f)) return ATTN_ERR_SCALE;
+  Strides st;
+  for (int i = 0; i < 12; ++i) st.v[i] = strides[i];
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, st, scale, causal, dtype, descale_q, descale_k,
+                    descale_v, stream);
 }
 
 int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num_splits, int* splits_used,
@@ -171,7 +236,8 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
   if (pl.workspace > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < pl.workspace))
     return ATTN_ERR_WORKSPACE;
   sdpa18::SplitParams sp;
-  sp.a = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, 128);
+  sp.a = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, 128, dense_strides(Hq, Hkv, Sq, Sk, d), 2,
+                     2);
   const size_t rows = (size_t)B * Hq * Sq;
   sp.part_o = pl.workspace > 0 ? static_cast<float*>(workspace) : nullptr;
   sp.part_lse = pl.workspace > 0 ? static_cast<float*>(workspace) + rows * pl.n_splits * (size_t)d : nullptr;
@@ -243,6 +309,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or smaller than the size query reports";
     case ATTN_ERR_SPLITS: return "num_splits must be in [0, 128]";
+    case ATTN_ERR_STRIDE:
+      return "a stride is negative, leaves rows overlapping or not 16-byte aligned, or spans 2 GiB within a head";
     default: return "unknown status";
   }
 }

@@ -88,10 +88,10 @@ constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource: 3
 // the kernel body, not from a lambda: the host pass rejects a device function
 // called from a lambda in a kernel template and then drops the launch stub.
 template <int NLOAD>
-__device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int seq_bytes,
+__device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int limit,
                                          const unsigned* off, unsigned char* dst) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + kt * tile_bytes), (short)0, seq_bytes - kt * tile_bytes, kBufferConfig);
+      (void*)(base + kt * tile_bytes), (short)0, limit - kt * tile_bytes, kBufferConfig);
 #pragma unroll
   for (int t = 0; t < NLOAD; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
@@ -138,11 +138,10 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   const int qw = q0 + wave * 32;
   const int qi = qw + i32;
 
-  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
-  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
-  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::RB;
-  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * C::RB;
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;  // lse row of query 0
+  const unsigned char* qbase = head_ptr(p.q, p.q_sb, p.q_sh, b, hq);
+  const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
+  const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
 
   const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
@@ -156,15 +155,15 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
 #pragma unroll
   for (int t = 0; t < C::DMA; ++t) {
     const int row = (64 * (C::DMA * wave + t) + lane) / C::CH;
-    kdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ k_swizzle<D>(row));
-    vdma_off[t] = row * C::RB + 16 * (dma_pchunk ^ v_swizzle<D>(row));
+    kdma_off[t] = row * p.k_ss + 16 * (dma_pchunk ^ k_swizzle<D>(row));
+    vdma_off[t] = row * p.v_ss + 16 * (dma_pchunk ^ v_swizzle<D>(row));
   }
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
   u32x4 qf[C::QS];
 #pragma unroll
   for (int s = 0; s < C::QS; ++s)
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * C::RB + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
 
   // ---- per-lane LDS operand offsets ------------------------------------------
   // K (A operand of S^T): row 32kb + i32, logical chunk 2s + g.
@@ -268,23 +267,26 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   };
 
   // ---- main loop: DMA of tile kt+1 overlaps compute of tile kt --------------
-  const int kv_bytes = p.Sk * C::RB;
+  // A tile of BN rows spans BN strides; the buffer of K (V) ends with the last
+  // key's row, so rows at or past Sk load as zeros.
+  const int k_tile = C::BN * p.k_ss, v_tile = C::BN * p.v_ss;
+  const int k_limit = (p.Sk - 1) * p.k_ss + C::RB, v_limit = (p.Sk - 1) * p.v_ss + C::RB;
   if (n_tiles > 0) {
-    dma_tile<C::DMA>(kbase, C::TILE, 0, kv_bytes, kdma_off, smem0 + 1024 * C::DMA * wave);
-    dma_tile<C::DMA>(vbase, C::TILE, 0, kv_bytes, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
+    dma_tile<C::DMA>(kbase, k_tile, 0, k_limit, kdma_off, smem0 + 1024 * C::DMA * wave);
+    dma_tile<C::DMA>(vbase, v_tile, 0, v_limit, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
   }
   __syncthreads();
   for (int kt = 0; kt < n_tiles; kt += 2) {
     if (kt + 1 < n_tiles) {
-      dma_tile<C::DMA>(kbase, C::TILE, kt + 1, kv_bytes, kdma_off, smem1 + 1024 * C::DMA * wave);
-      dma_tile<C::DMA>(vbase, C::TILE, kt + 1, kv_bytes, vdma_off, smem1 + C::TILE + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(kbase, k_tile, kt + 1, k_limit, kdma_off, smem1 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, v_tile, kt + 1, v_limit, vdma_off, smem1 + C::TILE + 1024 * C::DMA * wave);
     }
     if (kt < wave_tiles) compute_tile(kt, smem0);
     __syncthreads();
     if (kt + 1 >= n_tiles) break;
     if (kt + 2 < n_tiles) {
-      dma_tile<C::DMA>(kbase, C::TILE, kt + 2, kv_bytes, kdma_off, smem0 + 1024 * C::DMA * wave);
-      dma_tile<C::DMA>(vbase, C::TILE, kt + 2, kv_bytes, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(kbase, k_tile, kt + 2, k_limit, kdma_off, smem0 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, v_tile, kt + 2, v_limit, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
     }
     if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem1);
     __syncthreads();
@@ -295,7 +297,7 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run);
   if (qi >= p.Sq) return;
   const float inv = 1.0f / l_tot;
-  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)C::RB;
+  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll

@@ -82,10 +82,10 @@ __device__ __forceinline__ int v_swizzle(int row) { return (0xCA60 >> (4 * (row 
 // of load t filling the 16 bytes at dst + 1024 t + 16 l. The tile is read
 // through a raw buffer that starts at its first row and ends at the end of
 // the sequence, so rows at or past Sk fall outside it and load as zeros.
-__device__ __forceinline__ void dma_tile(const unsigned char* base, int kt, int seq_bytes, const unsigned* off,
-                                         unsigned char* dst) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * TILE), (short)0, seq_bytes - kt * TILE, kBufferConfig);
+__device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int limit,
+                                         const unsigned* off, unsigned char* dst) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(base + kt * tile_bytes), (short)0, limit - kt * tile_bytes, kBufferConfig);
 #pragma unroll
   for (int t = 0; t < DMA; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
@@ -150,12 +150,14 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const int qw = q0 + row_block * 32;
   const int qi = qw + i32;
 
-  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
-  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * RB;
-  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * RB;
-  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * RB;
-  const int kv_bytes = p.Sk * RB;
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;  // lse row of query 0
+  const unsigned char* qbase = head_ptr(p.q, p.q_sb, p.q_sh, b, hq);
+  const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
+  const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
+  // A tile of BN rows spans BN strides; the buffer of K (V) ends with the last
+  // key's row, so rows at or past Sk load as zeros.
+  const int k_tile = BN * p.k_ss, v_tile = BN * p.v_ss;
+  const int k_limit = (p.Sk - 1) * p.k_ss + RB, v_limit = (p.Sk - 1) * p.v_ss + RB;
 
   const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;  // tiles any wave of the workgroup needs
@@ -169,8 +171,8 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
 #pragma unroll
   for (int t = 0; t < DMA; ++t) {
     const int row = (64 * (DMA * wave + t) + lane) / CH;
-    kdma_off[t] = row * RB + 16 * (dma_pchunk ^ k_swizzle(row));
-    vdma_off[t] = row * RB + 16 * (dma_pchunk ^ v_swizzle(row));
+    kdma_off[t] = row * p.k_ss + 16 * (dma_pchunk ^ k_swizzle(row));
+    vdma_off[t] = row * p.v_ss + 16 * (dma_pchunk ^ v_swizzle(row));
   }
   const int dma_dst = 1024 * DMA * wave;
 
@@ -179,7 +181,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   u32x4 qf[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s)
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * RB + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
 
   int k_rd[QS];
 #pragma unroll
@@ -326,13 +328,13 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
 
   // DMA issued at the start of global phase 2n: K(n+1) and V(n).
   auto dma_phase = [&](int n, unsigned char* k_dst, unsigned char* v_dst) {
-    if (n + 1 < n_tiles) dma_tile(kbase, n + 1, kv_bytes, kdma_off, k_dst + dma_dst);
-    if (n < n_tiles) dma_tile(vbase, n, kv_bytes, vdma_off, v_dst + dma_dst);
+    if (n + 1 < n_tiles) dma_tile(kbase, k_tile, n + 1, k_limit, kdma_off, k_dst + dma_dst);
+    if (n < n_tiles) dma_tile(vbase, v_tile, n, v_limit, vdma_off, v_dst + dma_dst);
   };
 
   // ---- prologue: K(0) into slot 0 and V slot 1 zeroed (read by M(0)),
   // published before phase 0 ----------------------------------------------------
-  if (n_tiles > 0) dma_tile(kbase, 0, kv_bytes, kdma_off, k_lds0 + dma_dst);
+  if (n_tiles > 0) dma_tile(kbase, k_tile, 0, k_limit, kdma_off, k_lds0 + dma_dst);
 #pragma unroll
   for (int t = 0; t < TILE / (16 * 64 * WAVES); ++t)
     *(u32x4*)(v_lds1 + 16 * (tid + 64 * WAVES * t)) = u32x4{0, 0, 0, 0};
@@ -385,7 +387,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run);
   if (qi >= p.Sq) return;
   const float inv = 1.0f / l_tot;
-  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)RB;
+  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll

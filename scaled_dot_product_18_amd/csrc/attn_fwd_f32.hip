@@ -44,11 +44,10 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   const int qw = q0 + wave * 32;
   const int qi = qw + i32;
 
-  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
-  const float* qbase = (const float*)p.q + qo_row0 * D;
-  const float* kbase = (const float*)p.k + kv_row0 * D;
-  const float* vbase = (const float*)p.v + kv_row0 * D;
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;  // lse row of query 0
+  const unsigned char* qbase = head_ptr(p.q, p.q_sb, p.q_sh, b, hq);
+  const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
+  const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
 
   const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;
@@ -58,7 +57,7 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   // Q fragment (B operand of S^T): step s, half g holds dim 2s + g.
   float qf[D / 2];
 #pragma unroll
-  for (int s = 0; s < D / 2; ++s) qf[s] = (qi < p.Sq) ? qbase[(size_t)qi * D + 2 * s + g] : 0.f;
+  for (int s = 0; s < D / 2; ++s) qf[s] = (qi < p.Sq) ? ((const float*)(qbase + (size_t)qi * p.q_ss))[2 * s + g] : 0.f;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -78,8 +77,8 @@ void attn_fwd_f32_kernel(const AttnParams p) {
       const int kr = kv0 + row;
       float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
       if (kr < p.Sk) {
-        kx = *(const float4*)(kbase + (size_t)kr * D + 4 * c4);
-        vx = *(const float4*)(vbase + (size_t)kr * D + 4 * c4);
+        kx = *(const float4*)(kbase + (size_t)kr * p.k_ss + 16 * c4);
+        vx = *(const float4*)(vbase + (size_t)kr * p.v_ss + 16 * c4);
       }
       float* kd = ks + row * KLD + 4 * c4;
       kd[0] = kx.x;
@@ -140,7 +139,7 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run);
   if (qi >= p.Sq) return;
   const float inv = 1.0f / l_tot;
-  float* orow = (float*)p.o + (qo_row0 + qi) * D;
+  float* orow = (float*)((unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll

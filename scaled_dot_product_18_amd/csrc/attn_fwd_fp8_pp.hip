@@ -115,12 +115,14 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   const int qw = q0 + row_block * 32;
   const int qi = qw + i32;
 
-  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
-  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * KRB;
-  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * KRB;
-  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * KRB;
-  const int kv_bytes = p.Sk * KRB;
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;  // lse row of query 0
+  const unsigned char* qbase = head_ptr(p.q, p.q_sb, p.q_sh, b, hq);
+  const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
+  const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
+  // A tile of BN rows spans BN strides; the buffer of K (V) ends with the last
+  // key's row, so rows at or past Sk load as zeros.
+  const int k_tile = BN * p.k_ss, v_tile = BN * p.v_ss;
+  const int k_limit = (p.Sk - 1) * p.k_ss + KRB, v_limit = (p.Sk - 1) * p.v_ss + KRB;
 
   const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;
@@ -131,11 +133,11 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   // ---- K DMA: wave w fills rows 8w .. 8w+7 of a K tile (lane l: row 8w + l/8,
   // physical chunk l%8) ------------------------------------------------------
   const int kdma_row = 8 * wave + (lane >> 3);
-  const unsigned kdma_off = kdma_row * KRB + 16 * ((lane & 7) ^ swz(kdma_row));
+  const unsigned kdma_off = kdma_row * p.k_ss + 16 * ((lane & 7) ^ swz(kdma_row));
   const int kdma_dst = 1024 * wave;
   auto dma_k = [&](int kt, unsigned char* dst) {
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + kt * KTILE), (short)0, kv_bytes - kt * KTILE, kBufferConfig);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + kt * k_tile), (short)0, k_limit - kt * k_tile, kBufferConfig);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kdma_dst), 16, kdma_off, 0, 0, 0);
   };
 
@@ -145,9 +147,9 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   uint32_t vreg[4];
   auto load_v = [&](int kt) {
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + kt * KTILE), (short)0, kv_bytes - kt * KTILE, kBufferConfig);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + kt * v_tile), (short)0, v_limit - kt * v_tile, kBufferConfig);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vreg[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (4 * vkg + j) * KRB + vd0, 0, 0);
+    for (int j = 0; j < 4; ++j) vreg[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (4 * vkg + j) * p.v_ss + vd0, 0, 0);
   };
   // e4m3 -> bf16 (exact) and the transposed store: dimension vd0 + e gets the
   // 4 keys' values as one 8-byte unit at key offset 4 vkg of its V^T row.
@@ -175,8 +177,8 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   for (int s = 0; s < QS; ++s) {
     u32x4 q0v = u32x4{0, 0, 0, 0}, q1v = u32x4{0, 0, 0, 0};
     if (qi < p.Sq) {
-      q0v = *(const u32x4*)(qbase + (size_t)qi * KRB + 64 * s + 32 * g);
-      q1v = *(const u32x4*)(qbase + (size_t)qi * KRB + 64 * s + 32 * g + 16);
+      q0v = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 64 * s + 32 * g);
+      q1v = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 64 * s + 32 * g + 16);
     }
     qf[s] = i32x8{(int)q0v[0], (int)q0v[1], (int)q0v[2], (int)q0v[3],
                   (int)q1v[0], (int)q1v[1], (int)q1v[2], (int)q1v[3]};
@@ -385,7 +387,7 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run);
   if (qi >= p.Sq) return;
   const float inv = p.o_scale / l_tot;
-  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)(D * 2);
+  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll

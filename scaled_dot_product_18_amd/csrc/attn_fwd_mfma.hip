@@ -84,11 +84,10 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   const int qw = q0 + wave * 32;  // first query row of this wave
   const int qi = qw + i32;        // this lane's query row
 
-  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-  const size_t kv_row0 = ((size_t)b * p.Hkv + hk) * (size_t)p.Sk;
-  const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::KRB;
-  const unsigned char* kbase = (const unsigned char*)p.k + kv_row0 * C::KRB;
-  const unsigned char* vbase = (const unsigned char*)p.v + kv_row0 * (size_t)(D * C::ES);
+  const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;  // lse row of query 0
+  const unsigned char* qbase = head_ptr(p.q, p.q_sb, p.q_sh, b, hq);
+  const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
+  const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
 
   const int kv_end = CAUSAL ? min(p.Sk, q0 + C::BM + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
@@ -101,7 +100,7 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 #pragma unroll
   for (int s = 0; s < C::QREGS; ++s) {
     const int byte = FP8 ? (64 * (s >> 1) + 32 * g + 16 * (s & 1)) : (32 * s + 16 * g);
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * C::KRB + byte) : u32x4{0, 0, 0, 0};
+    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + byte) : u32x4{0, 0, 0, 0};
   }
 
   // ---- staging assignment --------------------------------------------------
@@ -118,16 +117,16 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int t = 0; t < C::KPASS; ++t) {
       const int kr = kv0 + kr0 + t * C::KROWS_PER_PASS;
-      kreg[t] = (kr < p.Sk) ? *(const u32x4*)(kbase + (size_t)kr * C::KRB + 16 * kc_) : u32x4{0, 0, 0, 0};
+      kreg[t] = (kr < p.Sk) ? *(const u32x4*)(kbase + (size_t)kr * p.k_ss + 16 * kc_) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kr = kv0 + 4 * vu + t;
       if (FP8) {
-        u32x2 x = (kr < p.Sk) ? *(const u32x2*)(vbase + (size_t)kr * D + vd0) : u32x2{0, 0};
+        u32x2 x = (kr < p.Sk) ? *(const u32x2*)(vbase + (size_t)kr * p.v_ss + vd0) : u32x2{0, 0};
         vreg[t] = u32x4{x[0], x[1], 0, 0};
       } else {
-        vreg[t] = (kr < p.Sk) ? *(const u32x4*)(vbase + (size_t)kr * (D * 2) + 2 * vd0) : u32x4{0, 0, 0, 0};
+        vreg[t] = (kr < p.Sk) ? *(const u32x4*)(vbase + (size_t)kr * p.v_ss + 2 * vd0) : u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -294,7 +293,7 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run);
   if (qi >= p.Sq) return;
   const float inv = p.o_scale / l_tot;
-  unsigned char* orow = (unsigned char*)p.o + (qo_row0 + qi) * (size_t)(D * 2);
+  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll

@@ -16,8 +16,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Parameters of one launch, passed by value. Every tensor is dense row-major:
-// q/o [B,Hq,Sq,D], k/v [B,Hkv,Sk,D], lse [B,Hq,Sq].
+// Parameters of one launch, passed by value. q/o are [B,Hq,Sq,D] and k/v
+// [B,Hkv,Sk,D] with the byte strides below; lse is dense [B,Hq,Sq].
 struct AttnParams {
   const void* q;
   const void* k;
@@ -31,7 +31,18 @@ struct AttnParams {
   float o_scale;        // descale_v (1 unless fp8 inputs)
   int xcd_remap;        // 1: order workgroups so each XCD owns whole KV heads ((B*Hkv) % 8 == 0)
   int causal_off;       // Sk - Sq: under the causal mask query i sees keys j <= i + causal_off
+  // Byte strides of q, k, v, o between batches (sb), heads (sh) and sequence
+  // positions (ss); the d elements of one position are contiguous. The dense
+  // [B,H,S,d] layout has ss = d * element size, sh = S * ss, sb = H * sh; the
+  // pages' (B,T,N,H) layout has ss = N * d * element size, sh = d * element size.
+  long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_ss, k_ss, v_ss, o_ss;
 };
+
+// First byte of head h of batch b of a strided [B,H,S,d] tensor.
+__device__ __forceinline__ const unsigned char* head_ptr(const void* base, long long sb, long long sh, int b, int h) {
+  return (const unsigned char*)base + (long long)b * sb + (long long)h * sh;
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

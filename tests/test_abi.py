@@ -33,7 +33,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _header_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp8",
-                                   "attn_fwd_splitkv", "attn_fwd_splitkv_plan", "attn_strerror", "attn_version"]
+                                   "attn_fwd_splitkv", "attn_fwd_splitkv_plan", "attn_fwd_strided", "attn_strerror",
+                                   "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -177,6 +178,36 @@ def test_bwd_validation_errors(lib):
     assert call(ws_bytes=nbytes - 1) == -10
     assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 128)[0] == -3
     assert lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 96)[0] == -4
+
+
+def test_strided_validation_errors(lib):
+    """attn_fwd_strided rejects unusable strides (and the shared errors) before any HIP call."""
+    B, Hq, Hkv, S, d = 2, 4, 2, 8, 64
+    bshd_q = [S * Hq * d, d, Hq * d]
+    bshd_kv = [S * Hkv * d, d, Hkv * d]
+    good = bshd_q + bshd_kv + bshd_kv + bshd_q
+
+    def call(strides=good, dtype=1, d=d, dq=1.0, **kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=None, causal=0, scale=0.125)
+        a.update(kw)
+        return lib.attn_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], B, Hq, Hkv, S, S, d, strides,
+                                    a["scale"], a["causal"], dtype, dq, 1.0, 1.0, None)
+
+    def with_(i, x):
+        t = list(good)
+        t[i] = x
+        return t
+
+    assert call(with_(2, d - 8)) == -12          # overlapping rows of q
+    assert call(with_(5, -64)) == -12            # negative position stride of k
+    assert call(with_(1, 4)) == -12              # head stride of 8 bytes: rows not 16-byte aligned
+    assert call(with_(11, 1 << 30)) == -12       # a head of o spans more than 2 GiB
+    assert call(with_(0, -1)) == -12
+    assert call(dtype=0, dq=2.0) == -7           # descales other than 1 need fp8
+    assert call(q=None) == -1 and call(d=96) == -4 and call(dtype=5) == -6
+    assert call(causal=1, q=P + 4) == -8
+    raw = lib.load().attn_fwd_strided
+    assert raw(P, P, P, P, None, 1, 1, 1, 8, 8, 64, None, 0.1, 0, 1, 1.0, 1.0, 1.0, None) == -1
 
 
 def test_python_wrapper_rejects_cpu_tensors():
