@@ -361,71 +361,82 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   const int n_qt = (p.Sq + C::BT - 1) / C::BT;
 
   size_t qo_row0 = 0;
+  // One 64-query tile in three stages, so the matrix core has independent work
+  // while the vector unit turns scores into P and dS: S and dP of both 32-query
+  // blocks, then P and dS of both, then the dV and dK updates of both. A block
+  // of queries past Sq, or that sees none of this wave's keys under the mask,
+  // is masked to zero rather than skipped, keeping the stages branch-free.
   auto compute_tile = [&](int t, const unsigned char* ql, const unsigned char* ol, const float* stl) {
+    constexpr int NB = 2;
+    // S = Q K^T, dP = dO V^T: lane = key kj, register r on half g <-> query qb0 + 8(r/4) + 4g + r%4
+    f32x16 s[NB], dp[NB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qb0 = t * C::BT + 32 * qb;
-      if (qb0 >= p.Sq) continue;
-      if (CAUSAL && qb0 + 31 + off < kw) continue;  // no query of the block sees a key of this wave
-      // S = Q K^T, dP = dO V^T: lane = key kj, register r on half g <-> query qb0 + 8(r/4) + 4g + r%4
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qb = 0; qb < NB; ++qb) {
+      s[qb] = f32x16{};
+      dp[qb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < C::QS; ++st) {
         const u32x4 a = *(const u32x4*)(ql + 32 * qb * C::RB + q_rd[st]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, kf[st]),
-                                                    s, 0, 0, 0);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, kf[st]), s[qb], 0, 0, 0);
       }
 #pragma unroll
       for (int st = 0; st < C::QS; ++st) {
         const u32x4 a = *(const u32x4*)(ol + 32 * qb * C::RB + q_rd[st]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                     __builtin_bit_cast(bf16x8, vf[st]), dp, 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         __builtin_bit_cast(bf16x8, vf[st]), dp[qb], 0, 0, 0);
       }
-      const bool edge = (CAUSAL && kw + 31 > qb0 + off) || qb0 + 32 > p.Sq || kw + 32 > p.Sk;
-      // lse2 / delta of queries qb0 + 8m + 4g + (0..3): one 16-byte LDS read each
-      f32x4 l2v[4], dlv[4];
+    }
+    // P and dS operands: chunk kc, element e <-> query qb0 + 16kc + 8(e/4) + 4g + e%4
+    u32x4 pf[NB][2], dsf[NB][2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        l2v[m] = *(const f32x4*)(stl + 32 * qb + 8 * m + 4 * g);
-        dlv[m] = *(const f32x4*)(stl + C::BT + 32 * qb + 8 * m + 4 * g);
-      }
+    for (int qb = 0; qb < NB; ++qb) {
+      const int qb0 = t * C::BT + 32 * qb;
+      const bool edge = (CAUSAL && kw + 31 > qb0 + off) || qb0 + 32 > p.Sq || kw + 32 > p.Sk;
       float pr[16], ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = qb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float l2 = l2v[r >> 2][r & 3];
-        const float dl = dlv[r >> 2][r & 3];
-        float x = exp2_fast(__builtin_fmaf(s[r], c, -l2));
-        if (edge) {
-          const bool ok = qq < p.Sq && kj < p.Sk && (!CAUSAL || kj <= qq + off);
-          x = ok ? x : 0.f;
+      for (int m = 0; m < 4; ++m) {
+        // lse2 / delta of queries qb0 + 8m + 4g + (0..3): one 16-byte LDS read each
+        const f32x4 l2 = *(const f32x4*)(stl + 32 * qb + 8 * m + 4 * g);
+        const f32x4 dl = *(const f32x4*)(stl + C::BT + 32 * qb + 8 * m + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e;
+          float x = exp2_fast(__builtin_fmaf(s[qb][r], c, -l2[e]));
+          if (edge) {
+            const int qq = qb0 + 8 * m + 4 * g + e;
+            const bool ok = qq < p.Sq && kj < p.Sk && (!CAUSAL || kj <= qq + off);
+            x = ok ? x : 0.f;
+          }
+          pr[r] = x;
+          ds[r] = x * (dp[qb][r] - dl[e]);
         }
-        pr[r] = x;
-        ds[r] = x * (dp[r] - dl);
       }
-      // P and dS operands: chunk kc, element e <-> query qb0 + 16kc + 8(e/4) + 4g + e%4
-      u32x4 pf[2], dsf[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          pf[j][e2] = pack_bf16x2(pr[8 * j + 2 * e2], pr[8 * j + 2 * e2 + 1]);
-          dsf[j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
+          pf[qb][j][e2] = pack_bf16x2(pr[8 * j + 2 * e2], pr[8 * j + 2 * e2 + 1]);
+          dsf[qb][j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
         }
-      // dV^T += dO^T P,  dK^T += Q^T dS
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const int base = (32 * qb + 16 * kc) * C::RB + t_rd[db];
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ol + base, C::RB),
-                                                           __builtin_bit_cast(bf16x8, pf[kc]), dv[db], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8, pf[qb][kc]), dv[db], 0, 0, 0);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ql + base, C::RB),
-                                                           __builtin_bit_cast(bf16x8, dsf[kc]), dk[db], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8, dsf[qb][kc]), dk[db], 0, 0, 0);
         }
-    }
   };
 
+  // Whether any query of tile t sees a key of this wave (always, without the mask).
+  auto sees = [&](int t) { return !CAUSAL || t * C::BT + C::BT - 1 + off >= kw; };
   const int q_bytes = p.Sq * C::RB;
   unsigned char* const qd0 = q_lds0 + 1024 * C::DMA * wave;
   unsigned char* const od0 = o_lds0 + 1024 * C::DMA * wave;
@@ -452,7 +463,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
         dma_tile<C::DMA>(obase, C::TILE, t + 1, q_bytes, qdma, od1);
         if (wave < 2) dma_stat(stat, t + 1, st_bytes, lane, (unsigned char*)st_lds1 + st_dst);
       }
-      if (wave_active) compute_tile(t, q_lds0, o_lds0, st_lds0);
+      if (wave_active && sees(t)) compute_tile(t, q_lds0, o_lds0, st_lds0);
       __syncthreads();
       if (t + 1 >= n_qt) break;
       if (t + 2 < n_qt) {
@@ -460,7 +471,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
         dma_tile<C::DMA>(obase, C::TILE, t + 2, q_bytes, qdma, od0);
         if (wave < 2) dma_stat(stat, t + 2, st_bytes, lane, (unsigned char*)st_lds0 + st_dst);
       }
-      if (wave_active) compute_tile(t + 1, q_lds1, o_lds1, st_lds1);
+      if (wave_active && sees(t + 1)) compute_tile(t + 1, q_lds1, o_lds1, st_lds1);
       __syncthreads();
     }
   }
