@@ -293,20 +293,33 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------
+  // O = acc / l rounded to bf16. A lane holds 4-dim pieces of one query row,
+  // so the wave writes its 32-row tile to LDS (stage buffer 0 is idle after
+  // the last barrier; wave w takes rows [32w, 32w+32) of it) and reads it back
+  // as whole rows, so that each global store covers 1 KB of contiguous rows.
+  // 16-byte chunks are XOR-swizzled by row.
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
-  if (qi >= p.Sq) return;
   const float inv = 1.0f / l_tot;
-  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
+  unsigned char* stage = smem0 + wave * (32 * C::RB);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * g;  // registers 4q4..4q4+3 hold dims d..d+3
-      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
-                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+      const int chunk = 4 * db + q4;  // dims 32 db + 8 q4 + [0, 8); this lane's 4 of them start at 4 g
+      *(u32x2*)(stage + i32 * C::RB + 16 * (chunk ^ (i32 & (C::CH - 1))) + 8 * g) =
+          u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
     }
-  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  unsigned char* obase = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq);
+  const int pchunk = lane % C::CH;
+#pragma unroll
+  for (int t = 0; t < 32 * C::RB / 1024; ++t) {
+    const int r = C::ROWS_PER_DMA * t + lane / C::CH;
+    const u32x4 val = *(const u32x4*)(stage + r * C::RB + 16 * pchunk);
+    if (qw + r < p.Sq) *(u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & (C::CH - 1)))) = val;
+  }
+  if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL>

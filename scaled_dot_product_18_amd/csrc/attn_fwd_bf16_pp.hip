@@ -45,6 +45,7 @@
 #include "kernel_common.h"
 #include "launch.h"
 
+
 namespace sdpa18 {
 namespace pp {
 
@@ -383,20 +384,34 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------
+  // O = acc / l rounded to bf16. A lane holds 4-dim pieces of one query row,
+  // so the wave first writes its 32 x 128 tile to LDS (the K/V slots are idle
+  // once the last barrier has passed; wave w takes 8 KB of slot w/2) and reads
+  // it back as whole rows: each global store then covers four 256-byte rows
+  // instead of 16 bytes of 32 rows. 16-byte chunks are XOR-swizzled by row.
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
-  if (qi >= p.Sq) return;
   const float inv = 1.0f / l_tot;
-  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
+  unsigned char* stage = (wave >> 1) == 0 ? k_lds0 : (wave >> 1) == 1 ? k_lds1 : (wave >> 1) == 2 ? v_lds0 : v_lds1;
+  stage += (wave & 1) * (32 * RB);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * g;
-      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
-                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+      const int chunk = 4 * db + q4;  // dims 32 db + 8 q4 + [0, 8); this lane's 4 of them start at 4 g
+      *(u32x2*)(stage + i32 * RB + 16 * (chunk ^ (i32 & 15)) + 8 * g) =
+          u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
     }
-  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
+  unsigned char* obase = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq);
+  const int pchunk = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 32 * RB / 1024; ++t) {
+    const int r = 4 * t + (lane >> 4);
+    const u32x4 val = *(const u32x4*)(stage + r * RB + 16 * pchunk);
+    if (qw + r < p.Sq) *(u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & 15))) = val;
+  }
+  if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace pp
