@@ -297,7 +297,8 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   // so the wave writes its 32-row tile to LDS (stage buffer 0 is idle after
   // the last barrier; wave w takes rows [32w, 32w+32) of it) and reads it back
   // as whole rows, so that each global store covers 1 KB of contiguous rows.
-  // 16-byte chunks are XOR-swizzled by row.
+  // 16-byte chunks are XOR-swizzled by row. The stores carry the non-temporal
+  // hint: nothing in the kernel reads O back.
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
   const float inv = 1.0f / l_tot;
@@ -317,7 +318,8 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   for (int t = 0; t < 32 * C::RB / 1024; ++t) {
     const int r = C::ROWS_PER_DMA * t + lane / C::CH;
     const u32x4 val = *(const u32x4*)(stage + r * C::RB + 16 * pchunk);
-    if (qw + r < p.Sq) *(u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & (C::CH - 1)))) = val;
+    if (qw + r < p.Sq)
+      __builtin_nontemporal_store(val, (u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & (C::CH - 1)))));
   }
   if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }

@@ -388,7 +388,8 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   // so the wave first writes its 32 x 128 tile to LDS (the K/V slots are idle
   // once the last barrier has passed; wave w takes 8 KB of slot w/2) and reads
   // it back as whole rows: each global store then covers four 256-byte rows
-  // instead of 16 bytes of 32 rows. 16-byte chunks are XOR-swizzled by row.
+  // instead of 16 bytes of 32 rows. 16-byte chunks are XOR-swizzled by row;
+  // the stores carry the non-temporal hint (nothing in the kernel reads O back).
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
   const float inv = 1.0f / l_tot;
@@ -409,7 +410,8 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   for (int t = 0; t < 32 * RB / 1024; ++t) {
     const int r = 4 * t + (lane >> 4);
     const u32x4 val = *(const u32x4*)(stage + r * RB + 16 * pchunk);
-    if (qw + r < p.Sq) *(u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & 15))) = val;
+    if (qw + r < p.Sq)
+      __builtin_nontemporal_store(val, (u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & 15))));
   }
   if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
 }
