@@ -383,20 +383,42 @@ void attn_fwd_fp8_pp_kernel(const AttnParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------
+  // O = descale_v * acc / l rounded to bf16. A lane holds 4-dim pieces of one
+  // query row, so each half of the wave's 32 rows is written to 4 KB of an
+  // idle V^T slot (no load or operand read is pending after the last barrier)
+  // and read back as whole rows: each global store then covers four 256-byte
+  // rows. 16-byte chunks are XOR-swizzled by row; the stores carry the
+  // non-temporal hint (nothing in the kernel reads O back).
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
-  if (qi >= p.Sq) return;
   const float inv = p.o_scale / l_tot;
-  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
+  constexpr int ORB = 2 * D;  // bytes per bf16 output row
+  unsigned char* stage = (wave < 4 ? v_lds0 : v_lds1) + (wave & 3) * (16 * ORB);
+  unsigned char* obase = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq);
+  const int pchunk = lane & 15;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int half = 0; half < 2; ++half) {
+    if ((i32 >> 4) == half) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * g;
-      *(u32x2*)(orow + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
-                                      pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int chunk = 4 * db + q4;  // dims 32 db + 8 q4 + [0, 8); this lane's 4 of them start at 4 g
+          *(u32x2*)(stage + (i32 & 15) * ORB + 16 * (chunk ^ (i32 & 15)) + 8 * g) =
+              u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                    pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
+        }
     }
-  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
+#pragma unroll
+    for (int t = 0; t < 16 * ORB / 1024; ++t) {
+      const int r = 4 * t + (lane >> 4);
+      const u32x4 val = *(const u32x4*)(stage + r * ORB + 16 * pchunk);
+      const int row = qw + 16 * half + r;
+      if (row < p.Sq)
+        __builtin_nontemporal_store(val, (u32x4*)(obase + (size_t)row * p.o_ss + 16 * (pchunk ^ r)));
+    }
+  }
+  if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_ref * c + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace fp8pp
