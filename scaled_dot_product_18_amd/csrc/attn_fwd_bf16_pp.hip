@@ -22,7 +22,7 @@
 // same number of key tiles.
 //
 // K/V tiles: K(n+1) and V(n) are loaded HBM -> LDS (buffer_load ... lds, 2 KB
-// per wave) at the start of global phase 2n and waited for before the barrier
+// per wave) during global phase 2n and waited for before the barrier
 // that ends phase 2n+1; K(m) is read in phases 2m (A) and 2m+1 (B), V(m-1)
 // likewise, so two K slots and two V slots suffice. The loop is unrolled over
 // four phases so that every slot is a fixed LDS object and the compiler can
@@ -44,6 +44,7 @@
 // would stall the partner wave's matrix core).
 #include "kernel_common.h"
 #include "launch.h"
+
 
 
 namespace sdpa18 {
@@ -343,7 +344,9 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
 
   // ---- global phases ----------------------------------------------------------
   // Global phase p ends with a barrier that waits for this wave's LDS reads
-  // and, when p is odd, for the DMA issued at the start of phase p-1.
+  // and, when p is odd, for the DMA issued in phase p-1. Group A issues its
+  // share of that DMA after the phase's MFMAs (its matrix work starts without
+  // waiting for the load issue), group B before its softmax.
   //   phase 4k   : DMA K(2k+1)->k1, V(2k)->v0 | A: M(2k)   [k0, v1] | B: V(2k-1)
   //   phase 4k+1 :                            | A: V(2k)            | B: M(2k)   [k0, v1]
   //   phase 4k+2 : DMA K(2k+2)->k0, V(2k+1)->v1 | A: M(2k+1) [k1, v0] | B: V(2k)
@@ -353,13 +356,13 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const int n_trips = (n_tiles + 2) / 2;  // covers M(0..n_tiles) and V(0..n_tiles-1)
   if (group == 0) {
     for (int k = 0; k < n_trips; ++k) {
-      dma_phase(2 * k, k_lds1, v_lds0);
       m_phase(2 * k, k_lds0, v_lds1);
+      dma_phase(2 * k, k_lds1, v_lds0);
       barrier_after<kWaitLgkm0>();
       v_phase(2 * k);
       barrier_after<kWaitVm0Lgkm0>();
-      dma_phase(2 * k + 1, k_lds0, v_lds1);
       m_phase(2 * k + 1, k_lds1, v_lds0);
+      dma_phase(2 * k + 1, k_lds0, v_lds1);
       barrier_after<kWaitLgkm0>();
       v_phase(2 * k + 1);
       barrier_after<kWaitVm0Lgkm0>();
