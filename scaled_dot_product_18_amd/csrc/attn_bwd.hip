@@ -107,6 +107,36 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* p, int rb) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Stores a wave's 32-row output tile, scaled by sc and rounded to bf16. Lane
+// (i32, g) holds dims 32 db + 8 q4 + 4 g + [0, 4) of tile row i32 in acc[db]
+// registers 4 q4 .. 4 q4 + 3, so the wave first writes the tile to its 32 * RB
+// bytes of LDS (16-byte chunks XOR-swizzled by row) and reads it back as whole
+// rows: each global store then covers 1 KB of contiguous rows instead of 16
+// bytes of 32 rows. Rows at or past n_rows are not stored; the stores carry
+// the non-temporal hint.
+template <int D>
+__device__ __forceinline__ void store_tile(const f32x16* acc, float sc, unsigned char* stage, unsigned char* out,
+                                           int n_rows, int lane) {
+  constexpr int RB = 2 * D, CH = RB / 16;
+  const int i32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int chunk = 4 * db + q4;
+      *(u32x2*)(stage + i32 * RB + 16 * (chunk ^ (i32 & (CH - 1))) + 8 * g) =
+          u32x2{pack_bf16x2(acc[db][4 * q4] * sc, acc[db][4 * q4 + 1] * sc),
+                pack_bf16x2(acc[db][4 * q4 + 2] * sc, acc[db][4 * q4 + 3] * sc)};
+    }
+  const int pchunk = lane % CH;
+#pragma unroll
+  for (int t = 0; t < 32 * RB / 1024; ++t) {
+    const int r = (1024 / RB) * t + lane / CH;
+    const u32x4 val = *(const u32x4*)(stage + r * RB + 16 * pchunk);
+    if (r < n_rows) __builtin_nontemporal_store(val, (u32x4*)(out + (size_t)r * RB + 16 * (pchunk ^ (r & (CH - 1)))));
+  }
+}
+
 // ---------------------------------------------------------------- delta
 // delta[row] = sum_c dO[row, c] * O[row, c] and lse2[row] = lse[row] * log2(e);
 // D/8 lanes per row, 8 elements each.
@@ -281,17 +311,11 @@ void attn_bwd_dq_kernel(const BwdParams p) {
     __syncthreads();
   }
 
-  if (!wave_active || qi >= p.Sq) return;
-  unsigned char* row = (unsigned char*)p.dq + (qo_row0 + qi) * C::RB;
-  const float sc = p.scale;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * g;  // registers 4q4..4q4+3 hold dims d..d+3
-      *(u32x2*)(row + 2 * d) = u32x2{pack_bf16x2(acc[db][4 * q4] * sc, acc[db][4 * q4 + 1] * sc),
-                                     pack_bf16x2(acc[db][4 * q4 + 2] * sc, acc[db][4 * q4 + 3] * sc)};
-    }
+  // dQ = scale * acc. The K/V tiles are idle after the last barrier: wave w
+  // stages its 32 rows in 32 * RB bytes of them.
+  if (!wave_active) return;
+  unsigned char* stage = (wave < 2 ? k_lds0 : v_lds0) + (wave & 1) * (32 * C::RB);
+  store_tile<D>(acc, p.scale, stage, (unsigned char*)p.dq + (qo_row0 + qw) * C::RB, p.Sq - qw, lane);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -476,20 +500,15 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     }
   }
 
-  if (!wave_active || kj >= p.Sk) return;
-  unsigned char* krow = (unsigned char*)p.dk + (kv_row0 + kj) * C::RB;
-  unsigned char* vrow = (unsigned char*)p.dv + (kv_row0 + kj) * C::RB;
-  const float sc = p.scale;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * db + 8 * q4 + 4 * g;
-      *(u32x2*)(krow + 2 * d) = u32x2{pack_bf16x2(dk[db][4 * q4] * sc, dk[db][4 * q4 + 1] * sc),
-                                      pack_bf16x2(dk[db][4 * q4 + 2] * sc, dk[db][4 * q4 + 3] * sc)};
-      *(u32x2*)(vrow + 2 * d) = u32x2{pack_bf16x2(dv[db][4 * q4], dv[db][4 * q4 + 1]),
-                                      pack_bf16x2(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3])};
-    }
+  // dK = scale * dk, dV = dv. The Q and dO tiles are idle after the last
+  // barrier: wave w stages its 32 dK rows in the Q tiles and its dV rows in the
+  // dO tiles.
+  if (!wave_active) return;
+  const int half = (wave & 1) * (32 * C::RB);
+  store_tile<D>(dk, p.scale, (wave < 2 ? q_lds0 : q_lds1) + half, (unsigned char*)p.dk + (kv_row0 + kw) * C::RB,
+                p.Sk - kw, lane);
+  store_tile<D>(dv, 1.0f, (wave < 2 ? o_lds0 : o_lds1) + half, (unsigned char*)p.dv + (kv_row0 + kw) * C::RB,
+                p.Sk - kw, lane);
 }
 
 template <int D, bool CAUSAL>
