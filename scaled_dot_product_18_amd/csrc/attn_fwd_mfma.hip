@@ -289,22 +289,35 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   }
 
   // ---- epilogue: normalise, round to bf16, store O (and lse) ---------------
+  // A lane holds 4-dim pieces of one query row, so the wave writes its 32-row
+  // output tile to LDS (idle after the last barrier; wave w takes 32 * 2D
+  // bytes) and reads it back as whole rows: each global store then covers 1 KB
+  // of contiguous rows. 16-byte chunks are XOR-swizzled by row; the stores
+  // carry the non-temporal hint (nothing in the kernel reads O back).
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
-  if (qi >= p.Sq) return;
   const float inv = p.o_scale / l_tot;
-  unsigned char* orow = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq) + (size_t)qi * p.o_ss;
+  constexpr int ORB = 2 * D, OCH = ORB / 16;
+  unsigned char* stage = smem + wave * (32 * ORB);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      // registers 4*q4 .. 4*q4+3 hold dims 32db + 8q4 + 4g + 0..3
-      const int d = 32 * db + 8 * q4 + 4 * g;
-      u32x2 val = u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
-                        pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
-      *(u32x2*)(orow + 2 * d) = val;
+      const int chunk = 4 * db + q4;  // dims 32 db + 8 q4 + [0, 8); this lane's 4 of them start at 4 g
+      *(u32x2*)(stage + i32 * ORB + 16 * (chunk ^ (i32 & (OCH - 1))) + 8 * g) =
+          u32x2{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)};
     }
-  if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  unsigned char* obase = (unsigned char*)head_ptr(p.o, p.o_sb, p.o_sh, b, hq);
+  const int pchunk = lane % OCH;
+#pragma unroll
+  for (int t = 0; t < 32 * ORB / 1024; ++t) {
+    const int r = (1024 / ORB) * t + lane / OCH;
+    const u32x4 val = *(const u32x4*)(stage + r * ORB + 16 * pchunk);
+    if (qw + r < p.Sq)
+      __builtin_nontemporal_store(val, (u32x4*)(obase + (size_t)(qw + r) * p.o_ss + 16 * (pchunk ^ (r & (OCH - 1)))));
+  }
+  if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool FP8>
