@@ -204,10 +204,14 @@ int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num
  *             query heads, computed without atomics);
  *   dtype     ATTN_BF16 only: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse;
  *   workspace device memory owned by the caller, 16-byte aligned, at least
- *             attn_bwd_workspace_size bytes (2*B*Hq*Sq floats: the per-row
- *             rowsum(dout * O), then lse * log2(e)); contents on entry
- *             ignored, unspecified on return; two calls in flight need two
- *             workspaces.
+ *             attn_bwd_workspace_size bytes: 2*B*Hq*Sq floats (the per-row
+ *             rowsum(dout * O), then lse * log2(e)), and, when the query
+ *             heads of a KV head are split into s > 1 subsets (groups of 8 or
+ *             more heads on grids under 512 dK/dV workgroups, e.g. MQA), from
+ *             the next 16-byte boundary the fp32 partial dK and dV of every
+ *             subset (2*s*B*Hkv*Sk*d floats), summed in subset order;
+ *             contents on entry ignored, unspecified on return; two calls in
+ *             flight need two workspaces.
  *   Other arguments as attn_fwd.
  *
  * Returns ATTN_OK or a negative status: ATTN_ERR_NULL if any of q, k, v, o,

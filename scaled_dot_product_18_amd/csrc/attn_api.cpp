@@ -107,6 +107,16 @@ sdpa18::AttnParams make_params(const void* q, const void* k, const void* v, void
 
 int launch_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// Workspace of attn_bwd: per-row delta and lse * log2(e) (2 * B*Hq*Sq floats),
+// then, when the dK/dV kernel splits the query heads of a KV head, 16-byte
+// aligned fp32 partial dK and dV of every subset.
+size_t bwd_part_offset(int B, int Hq, int Sq) { return (2 * (size_t)B * Hq * Sq * sizeof(float) + 15) / 16 * 16; }
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
+  const int ks = sdpa18::bwd_kv_split(B, Hkv, Sk, Hq / Hkv);
+  if (ks == 1) return 2 * (size_t)B * Hq * Sq * sizeof(float);
+  return bwd_part_offset(B, Hq, Sq) + 2 * (size_t)ks * B * Hkv * Sk * d * sizeof(float);
+}
+
 constexpr int kMaxSplits = 128;
 
 // Checks of attn_fwd_splitkv_plan and attn_fwd_splitkv beyond the shared ones.
@@ -251,7 +261,7 @@ int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
   if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  if (workspace_bytes != nullptr) *workspace_bytes = 2 * (size_t)B * Hq * Sq * sizeof(float);
+  if (workspace_bytes != nullptr) *workspace_bytes = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
   return ATTN_OK;
 }
 
@@ -267,7 +277,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
   if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
   const size_t rows = (size_t)B * Hq * Sq;
-  const size_t need = 2 * rows * sizeof(float);
+  const size_t need = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   sdpa18::BwdParams bp;
   bp.q = q;
@@ -292,6 +302,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   bp.qk_scale_log2 = scale * kLog2e;
   bp.n_qtiles = (Sq + 127) / 128;
   bp.n_ktiles = (Sk + 127) / 128;
+  bp.kv_split = sdpa18::bwd_kv_split(B, Hkv, Sk, Hq / Hkv);
+  bp.dkv_part = bp.kv_split > 1
+                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bwd_part_offset(B, Hq, Sq))
+                    : nullptr;
   return launch_status(sdpa18::launch_attn_bwd_bf16(bp, d, causal != 0, stream));
 }
 

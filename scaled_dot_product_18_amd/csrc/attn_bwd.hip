@@ -337,11 +337,16 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   const int i32 = lane & 31;
   const int g = lane >> 5;
 
+  // Work item (key tile, query-head subset, batch, KV head), key tiles
+  // ascending: under the mask the first keys see the most queries.
   const int BH = p.B * p.Hkv;
-  const int kt = blockIdx.x / BH;  // ascending: under the mask the first keys see the most queries
-  const int rem = blockIdx.x - kt * BH;
+  const int kt = blockIdx.x / (BH * p.kv_split);
+  int rem = blockIdx.x - kt * BH * p.kv_split;
+  const int sp = rem / BH;  // query-head subset
+  rem -= sp * BH;
   const int b = rem / p.Hkv;
   const int hk = rem - b * p.Hkv;
+  const int heads = p.group / p.kv_split;
 
   const int k0 = kt * 128;
   const int kw = k0 + 32 * wave;
@@ -466,7 +471,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   unsigned char* const od0 = o_lds0 + 1024 * C::DMA * wave;
   unsigned char* const qd1 = q_lds1 + 1024 * C::DMA * wave;
   unsigned char* const od1 = o_lds1 + 1024 * C::DMA * wave;
-  for (int gq = 0; gq < p.group; ++gq) {
+  for (int gq = sp * heads; gq < (sp + 1) * heads; ++gq) {
     const int hq = hk * p.group + gq;
     qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
     const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
@@ -500,15 +505,56 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     }
   }
 
+  if (!wave_active) return;
+  if (p.kv_split > 1) {
+    // This subset's fp32 partial sums; attn_bwd_dkdv_reduce_kernel adds the
+    // subsets in index order. Lane (i32, g) holds dims 32 db + 8 q4 + 4 g + [0, 4).
+    if (kj >= p.Sk) return;
+    const size_t rows = (size_t)p.B * p.Hkv * p.Sk;
+    float* pk = p.dkv_part + ((size_t)sp * rows + kv_row0 + kj) * D;
+    float* pv = pk + (size_t)p.kv_split * rows * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * db + 8 * q4 + 4 * g;
+        *(float4*)(pk + d) = float4{dk[db][4 * q4] * p.scale, dk[db][4 * q4 + 1] * p.scale,
+                                    dk[db][4 * q4 + 2] * p.scale, dk[db][4 * q4 + 3] * p.scale};
+        *(float4*)(pv + d) = float4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+      }
+    return;
+  }
   // dK = scale * dk, dV = dv. The Q and dO tiles are idle after the last
   // barrier: wave w stages its 32 dK rows in the Q tiles and its dV rows in the
   // dO tiles.
-  if (!wave_active) return;
   const int half = (wave & 1) * (32 * C::RB);
   store_tile<D>(dk, p.scale, (wave < 2 ? q_lds0 : q_lds1) + half, (unsigned char*)p.dk + (kv_row0 + kw) * C::RB,
                 p.Sk - kw, lane);
   store_tile<D>(dv, 1.0f, (wave < 2 ? o_lds0 : o_lds1) + half, (unsigned char*)p.dv + (kv_row0 + kw) * C::RB,
                 p.Sk - kw, lane);
+}
+
+// dK and dV from the fp32 partials of the query-head subsets, summed in
+// subset order (deterministic) and rounded to bf16; 8 dims per thread.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_bwd_dkdv_reduce_kernel(const BwdParams p,
+                                                                                                   int d) {
+  const size_t n8 = (size_t)p.B * p.Hkv * p.Sk * d / 8;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t part = n8 * 8;  // floats per subset and tensor
+  for (int tensor = 0; tensor < 2; ++tensor) {
+    const float* src = p.dkv_part + (size_t)tensor * p.kv_split * part + 8 * i;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < p.kv_split; ++sp) {
+      const float4 a = *(const float4*)(src + sp * part);
+      const float4 b = *(const float4*)(src + sp * part + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    unsigned char* dst = (unsigned char*)(tensor == 0 ? p.dk : p.dv) + 16 * i;
+    *(u32x4*)dst = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                         pack_bf16x2(acc[6], acc[7])};
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -523,8 +569,15 @@ hipError_t launch_d(const BwdParams& bp, hipStream_t stream) {
   e = hipLaunchKernel((const void*)&attn_bwd_dq_kernel<D, CAUSAL>,
                       dim3((unsigned)bp.n_qtiles * (unsigned)bp.B * (unsigned)bp.Hq), dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)&attn_bwd_dkdv_kernel<D, CAUSAL>,
-                         dim3((unsigned)bp.n_ktiles * (unsigned)bp.B * (unsigned)bp.Hkv), dim3(256), args, 0, stream);
+  e = hipLaunchKernel((const void*)&attn_bwd_dkdv_kernel<D, CAUSAL>,
+                      dim3((unsigned)bp.n_ktiles * (unsigned)bp.B * (unsigned)bp.Hkv * (unsigned)bp.kv_split),
+                      dim3(256), args, 0, stream);
+  if (e != hipSuccess || bp.kv_split == 1) return e;
+  int d = D;
+  void* rargs[] = {&arg, &d};
+  const size_t n8 = (size_t)bp.B * bp.Hkv * bp.Sk * D / 8;
+  return hipLaunchKernel((const void*)&attn_bwd_dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256),
+                         rargs, 0, stream);
 }
 
 }  // namespace bwd

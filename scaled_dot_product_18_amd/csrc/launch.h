@@ -68,8 +68,20 @@ struct BwdParams {
   float scale;          // multiplier of the dot products
   float qk_scale_log2;  // scale * log2(e)
   int n_qtiles;         // ceil(Sq / 128): dQ workgroups per (batch, query head)
-  int n_ktiles;         // ceil(Sk / 128): dK/dV workgroups per (batch, KV head)
+  int n_ktiles;         // ceil(Sk / 128): dK/dV workgroups per (batch, KV head) and query-head subset
+  int kv_split;         // query-head subsets per KV head in the dK/dV kernel (1: no partial sums)
+  float* dkv_part;      // workspace, kv_split > 1 only: fp32 dK then dV partials [2][kv_split][B*Hkv*Sk][d]
 };
+
+// Query-head subsets per KV head for the dK/dV kernel: doubled while the grid
+// is under two rounds of 256 workgroups and every subset keeps at least four
+// query heads (MQA at long sequences would otherwise leave CUs idle).
+inline int bwd_kv_split(int B, int Hkv, int Sk, int group) {
+  const long long base = (long long)((Sk + 127) / 128) * B * Hkv;
+  int ks = 1;
+  while (base * ks < 512 && group % (2 * ks) == 0 && group / (2 * ks) >= 4) ks *= 2;
+  return ks;
+}
 
 // bf16, d in {64, 128}: delta, then dQ, then dK and dV, on one stream.
 hipError_t launch_attn_bwd_bf16(const BwdParams& bp, int d, bool causal, hipStream_t stream);

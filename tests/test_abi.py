@@ -176,6 +176,12 @@ def test_bwd_validation_errors(lib):
     st, nbytes = lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 128)
     assert st == 0 and nbytes == 2 * 4 * 8 * 4
     assert call(ws_bytes=nbytes - 1) == -10
+    # MQA with 8 query heads: the dK/dV kernel splits them into 2 subsets of 4, whose
+    # fp32 partial dK and dV follow the 16-byte aligned row statistics.
+    st, nbytes = lib.attn_bwd_workspace_size(1, 8, 1, 8, 8, 128)
+    assert st == 0 and nbytes == 2 * 8 * 8 * 4 + 2 * 2 * 8 * 128 * 4
+    st, nbytes = lib.attn_bwd_workspace_size(1, 4, 1, 8, 8, 128)  # 4 heads: no split
+    assert st == 0 and nbytes == 2 * 4 * 8 * 4
     assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 128)[0] == -3
     assert lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 96)[0] == -4
 

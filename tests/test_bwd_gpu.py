@@ -57,6 +57,19 @@ def test_bwd_tails(gpu, S, d, causal, heads):
     log(f"  {stats}")
 
 
+# Groups of 8 and 16 query heads per KV head: the dK/dV kernel splits them into
+# 2 and 4 subsets whose fp32 partial sums a second kernel adds.
+SPLIT_HEADS = [(8, 1), (16, 1), (16, 2)]
+
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([17, 129, 257], (64, 128), (False, True),
+                                                                    SPLIT_HEADS)))
+def test_bwd_query_head_subsets(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    stats, *_ = _run(sdpa_inputs.custom(2, Hq, Hkv, S, S, d, "bf16", causal, seed=14000 + S + Hq))
+    log(f"  {stats}")
+
+
 @pytest.mark.parametrize("Sq,Sk,d", [(1, 300, 128), (5, 64, 64), (77, 200, 128), (130, 257, 64), (256, 1000, 128)])
 def test_bwd_queries_are_the_last_positions(gpu, Sq, Sk, d):
     """Causal with Sq < Sk (bottom-right mask), and the same shapes unmasked."""
