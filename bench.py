@@ -27,6 +27,8 @@ Other modes:
     --no-cpu-baseline        skip the oracle timing
     --copy-calibration MIB   run a plain device copy of MIB MiB (to calibrate HBM byte counters)
     --sweep                  the codelab's own benchmark shapes (one JSON line per shape, see sweep_shapes)
+    --eager                  time forward steps as K separate calls with events around each (default: one HIP
+                             graph of the K launches, replayed once)
 """
 
 from __future__ import annotations
@@ -243,6 +245,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--eager", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -283,7 +286,11 @@ def main() -> int:
         dev["dout"] = inp["dout"].cuda()
         dev["o"], dev["lse"] = sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale,
                                         want_lse=True)
-        workspace = torch.empty(2 * w.B * w.Hq * w.Sq * 4, dtype=torch.uint8, device="cuda")
+        from scaled_dot_product_18_amd import _lib
+        st, nbytes = _lib.attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d)
+        if st != 0:
+            raise RuntimeError(f"attn_bwd_workspace_size: status {st}")
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
 
     def step():
         if w.path == "bwd":
@@ -303,25 +310,50 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    # Forward steps are timed as one HIP graph of K launches (the library only
+    # enqueues kernels on the caller's stream, so a graph captures them): from
+    # Python each call costs more host time than a short kernel runs, and the
+    # graph keeps the GPU fed. The replayed output must equal the eager one.
+    # The backward step allocates its gradients per call and is timed eagerly,
+    # with events around every launch.
+    use_graph = w.path != "bwd" and not args.eager
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    if use_graph:
+        eager_out = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager_out):
+            raise RuntimeError("the graph replay's output differs from the eager call's")
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {args.steps} steps" + (" (one graph replay)" if use_graph else ""))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     region0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
     region1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
 
     region_ms = region0.elapsed_time(region1)
-    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    if use_graph:
+        per_launch = [region_ms / args.steps]
+    else:
+        per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     avg_launch_ms = sum(per_launch) / len(per_launch)
     ms_per_step = region_ms / args.steps
     flops = w.flops()
@@ -374,6 +406,7 @@ def main() -> int:
         },
         "cpu_baseline": None,
         "kernel_source_sha": kernel_source_hash(kernel_name(w)),
+        "timing": "one HIP graph of the K launches, replayed once" if use_graph else "events around each of K launches",
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
