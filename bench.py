@@ -63,6 +63,7 @@ def log(msg: str) -> None:
 KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
                   "attn_fwd_fp8_pp_kernel": "attn_fwd_fp8_pp.hip",
                   "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip",
+                  "attn_fwd_f32_split_kernel": "attn_fwd_f32.hip",
                   "attn_fwd_splitkv_kernel": "attn_fwd_splitkv.hip", "attn_bwd_dkdv_kernel": "attn_bwd.hip"}
 SHARED_SOURCES = ("kernel_common.h", "launch.h", "attn_api.cpp")
 
@@ -88,6 +89,8 @@ def kernel_name(w) -> str:
         return "attn_fwd_bf16_pp_kernel"
     if w.dtype == "fp8" and w.d == 128:
         return "attn_fwd_fp8_pp_kernel"
+    if w.dtype == "f32" and (w.Sq + 127) // 128 * w.B * w.Hq < 64 and w.Sk > 32:
+        return "attn_fwd_f32_split_kernel"  # grids under 64 workgroups of 128 rows split the keys
     return {"f32": "attn_fwd_f32_kernel", "bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_mfma_kernel"}[w.dtype]
 
 
