@@ -60,6 +60,14 @@ def test_f32_tails(gpu, S, d, causal, heads):
     _run_full(sdpa_inputs.custom(2, Hq, Hkv, S, S, d, "f32", causal, seed=2000 + S))
 
 
+@pytest.mark.parametrize("B,H,S,d,causal", [(4, 8, 500, 64, False), (1, 8, 1000, 128, True), (4, 8, 1024, 64, True)])
+def test_f32_grid_sizes(gpu, B, H, S, d, causal):
+    """fp32 grids under and at one 128-row workgroup per CU (256): the first two run the
+    four-way key split with its LDS merge over many 128-key super-tiles, the last the
+    four-wave kernel. lse on."""
+    _run_full(sdpa_inputs.custom(B, H, H, S, S, d, "f32", causal, seed=2500 + S + d, want_lse=True))
+
+
 @pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 63, 64, 65, 129, 257], (64, 128),
                                                                     (False, True), HEADS)))
 def test_fp8_tails(gpu, S, d, causal, heads):
