@@ -89,8 +89,8 @@ def kernel_name(w) -> str:
         return "attn_fwd_bf16_pp_kernel"
     if w.dtype == "fp8" and w.d == 128:
         return "attn_fwd_fp8_pp_kernel"
-    if w.dtype == "f32" and (w.Sq + 127) // 128 * w.B * w.Hq < 256 and w.Sk > 32:
-        return "attn_fwd_f32_split_kernel"  # grids under 256 workgroups of 128 rows split the keys
+    if w.dtype == "f32" and (w.Sq + 127) // 128 * w.B * w.Hq <= 128 and w.Sk > 32:
+        return "attn_fwd_f32_split_kernel"  # grids up to 128 workgroups of 128 rows split the keys
     return {"f32": "attn_fwd_f32_kernel", "bf16": "attn_fwd_bf16_kernel", "fp8": "attn_fwd_mfma_kernel"}[w.dtype]
 
 

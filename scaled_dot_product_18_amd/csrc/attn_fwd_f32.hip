@@ -151,7 +151,7 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   if (g == 0 && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
-// Small grids (under 256 workgroups of 128 rows, e.g. one 128-token head): one
+// Small grids (up to 128 workgroups of 128 rows, e.g. one 128-token head): one
 // workgroup per 32 query rows, so the work spreads over four times as many CUs, and its 4
 // waves (one per SIMD) split the keys: keys arrive in super-tiles of 128 (one
 // load round trip for four 32-key tiles) and wave s runs the online softmax
@@ -341,10 +341,11 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   // hipLaunchKernel reports the status of this launch alone.
   AttnParams arg = p;
   void* args[] = {&arg};
-  // Under one workgroup per CU most matrix units sit idle: one workgroup per
-  // 32 query rows instead, its four waves splitting the keys. From 256
-  // workgroups up the four-wave kernel is the faster one (measured).
-  if (grid < 256 && p.Sk > 32) {
+  // Small grids leave most matrix units idle: one workgroup per 32 query rows
+  // instead, its four waves splitting the keys. Measured, the split is faster
+  // up to 128 workgroups of 128 rows and slower from 192 (at d = 128 one split
+  // workgroup fills a CU's LDS, so four times the grid takes several rounds).
+  if (grid <= 128 && p.Sk > 32) {
     arg.n_qtiles = (p.Sq + 31) / 32;
     const unsigned grid32 = (unsigned)arg.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
     return hipLaunchKernel((const void*)&attn_fwd_f32_split_kernel<D, CAUSAL>, dim3(grid32), dim3(256), args, 0,

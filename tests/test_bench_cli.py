@@ -27,7 +27,7 @@ def test_more_than_one_gpu_is_refused(argv, env):
 def test_kernel_names_follow_the_launch_dispatch():
     """The dominant kernel per workload, as the launchers pick it: the eight-wave
     ping-pong kernels at d=128, the four-wave kernels at d=64, the fp32 key-split
-    kernel for grids under 256 workgroups of 128 query rows."""
+    kernel for grids up to 128 workgroups of 128 query rows."""
     W = sdpa_inputs.WORKLOADS
     assert bench.kernel_name(W["single_head_f32_s128_d64"]) == "attn_fwd_f32_split_kernel"
     assert bench.kernel_name(W["vit_b16_bf16_b32_h12_s196_d64"]) == "attn_fwd_bf16_kernel"
@@ -35,10 +35,10 @@ def test_kernel_names_follow_the_launch_dispatch():
     assert bench.kernel_name(W["causal_fp8_b1_h32_s16384_d128"]) == "attn_fwd_fp8_pp_kernel"
     assert bench.kernel_name(W["decode_gqa_bf16_b4_hq32_hkv8_sk32768_d128"]) == "attn_fwd_splitkv_kernel"
     assert bench.kernel_name(W["bwd_causal_gqa_bf16_b4_hq32_hkv8_s4096_d128"]) == "attn_bwd_dkdv_kernel"
-    # the fp32 switch: 255 workgroups split the keys, 256 do not
+    # the fp32 switch: 128 workgroups split the keys, 129 do not
     f32 = lambda B, H, S: sdpa_inputs.custom(B, H, H, S, S, 64, "f32", False, seed=0)  # noqa: E731
-    assert bench.kernel_name(f32(1, 255, 128)) == "attn_fwd_f32_split_kernel"
-    assert bench.kernel_name(f32(1, 256, 128)) == "attn_fwd_f32_kernel"
+    assert bench.kernel_name(f32(1, 128, 128)) == "attn_fwd_f32_split_kernel"
+    assert bench.kernel_name(f32(1, 129, 128)) == "attn_fwd_f32_kernel"
     assert bench.kernel_name(f32(1, 1, 32)) == "attn_fwd_f32_kernel"  # one key tile: nothing to split
 
 
