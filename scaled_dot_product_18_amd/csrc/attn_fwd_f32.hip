@@ -9,13 +9,14 @@
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); KV
 // tiles of 32 keys go through one LDS buffer (K rows padded by one float so
-// the column reads of the S^T operand hit distinct banks).
+// the column reads of the S^T operand hit distinct banks), the next tile
+// waiting in registers meanwhile.
 #include "kernel_common.h"
 #include "launch.h"
 
 namespace sdpa18 {
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PREFETCH>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void attn_fwd_f32_kernel(const AttnParams p) {
   constexpr int BM = 128;
@@ -66,28 +67,46 @@ void attn_fwd_f32_kernel(const AttnParams p) {
   float l_run = 0.f;
   const float c = p.qk_scale_log2;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int kv0 = kt * BN;
-    __syncthreads();  // previous tile fully consumed
+  // PREFETCH: the next tile's K and V rows are loaded into registers while
+  // the current tile is computed, and written to LDS after the barrier that
+  // ends it. It costs 4 LOADS VGPRs: at d = 64 that lowers the resident waves
+  // per SIMD from three to two, which large grids feel more than the hidden
+  // load latency; without it each tile is loaded after the barrier.
+  float4 kx[LOADS], vx[LOADS];
+  auto load_tile = [&](int kt) {
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
       const int f = tid + 256 * t;
       const int row = f / (D / 4);
       const int c4 = f - row * (D / 4);
-      const int kr = kv0 + row;
-      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      const int kr = kt * BN + row;
+      kx[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      vx[t] = kx[t];
       if (kr < p.Sk) {
-        kx = *(const float4*)(kbase + (size_t)kr * p.k_ss + 16 * c4);
-        vx = *(const float4*)(vbase + (size_t)kr * p.v_ss + 16 * c4);
+        kx[t] = *(const float4*)(kbase + (size_t)kr * p.k_ss + 16 * c4);
+        vx[t] = *(const float4*)(vbase + (size_t)kr * p.v_ss + 16 * c4);
       }
+    }
+  };
+  if (PREFETCH && n_tiles > 0) load_tile(0);
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int kv0 = kt * BN;
+    __syncthreads();  // previous tile fully consumed
+    if (!PREFETCH) load_tile(kt);
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) {
+      const int f = tid + 256 * t;
+      const int row = f / (D / 4);
+      const int c4 = f - row * (D / 4);
       float* kd = ks + row * KLD + 4 * c4;
-      kd[0] = kx.x;
-      kd[1] = kx.y;
-      kd[2] = kx.z;
-      kd[3] = kx.w;
-      *(float4*)(vs + row * D + 4 * c4) = vx;
+      kd[0] = kx[t].x;
+      kd[1] = kx[t].y;
+      kd[2] = kx[t].z;
+      kd[3] = kx[t].w;
+      *(float4*)(vs + row * D + 4 * c4) = vx[t];
     }
     __syncthreads();
+    if (PREFETCH && kt + 1 < n_tiles) load_tile(kt + 1);
     if (kt >= wave_tiles) continue;
 
     // S^T = K . Q^T: row i = key kv0 + i, column = query of this lane.
@@ -351,7 +370,14 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
     return hipLaunchKernel((const void*)&attn_fwd_f32_split_kernel<D, CAUSAL>, dim3(grid32), dim3(256), args, 0,
                            stream);
   }
-  return hipLaunchKernel((const void*)&attn_fwd_f32_kernel<D, CAUSAL>, dim3(grid), dim3(256), args, 0, stream);
+  // Register prefetch of the next tile: always at d = 128 (one wave per SIMD
+  // either way), at d = 64 up to 256 workgroups (measured faster there, slower
+  // from 1024 up, where residency matters more).
+  if (D == 128 || grid <= 256)
+    return hipLaunchKernel((const void*)&attn_fwd_f32_kernel<D, CAUSAL, true>, dim3(grid), dim3(256), args, 0,
+                           stream);
+  return hipLaunchKernel((const void*)&attn_fwd_f32_kernel<D, CAUSAL, false>, dim3(grid), dim3(256), args, 0,
+                         stream);
 }
 
 int f32_block_m() { return 128; }

@@ -61,11 +61,12 @@ def test_f32_tails(gpu, S, d, causal, heads):
 
 
 @pytest.mark.parametrize("B,H,S,d,causal", [(4, 8, 500, 64, False), (1, 8, 1000, 128, True), (4, 32, 512, 128, False),
-                                            (4, 8, 1024, 64, True)])
+                                            (4, 8, 1024, 64, True), (2, 24, 700, 64, True)])
 def test_f32_grid_sizes(gpu, B, H, S, d, causal):
-    """fp32 grids of 32, 64, 128 and 256 workgroups of 128 rows: the first three run the
-    four-way key split with its LDS merge over many 128-key super-tiles, the last the
-    four-wave kernel. lse on."""
+    """fp32 grids of 32, 64, 128, 256 and 288 workgroups of 128 rows: the first three run
+    the four-way key split with its LDS merge over many 128-key super-tiles, 256 the
+    four-wave kernel with the next tile prefetched into registers, 288 (d = 64) the
+    four-wave kernel without it. lse on."""
     _run_full(sdpa_inputs.custom(B, H, H, S, S, d, "f32", causal, seed=2500 + S + d, want_lse=True))
 
 
