@@ -9,8 +9,10 @@
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); KV
 // tiles of 32 keys go through one LDS buffer (K rows padded by one float so
-// the column reads of the S^T operand hit distinct banks), the next tile
-// waiting in registers meanwhile.
+// the column reads of the S^T operand hit distinct banks); at d = 128, and
+// for grids up to 256 workgroups at d = 64, the next tile waits in registers
+// meanwhile. Grids of up to 128 workgroups run the key-split kernel further
+// down instead, one workgroup per 32 query rows.
 #include "kernel_common.h"
 #include "launch.h"
 
