@@ -23,6 +23,14 @@ workload whose arithmetic intensity is below the ridge point reports the HBM
 roofline (algorithmic bytes per launch over the launch time) instead of the
 matrix-core one.
 
+Before timing, --warmup calls run and then more calls until --warm-seconds
+(default 1 s) of launches have passed, so the clocks are those of a
+sustained run. The line also carries the distribution of single launches
+(median / min / p90, events around each call), the CU count and peak clock,
+the achieved clock and matrix-core / vector-unit / LDS utilisation from the
+committed counter summary of the same kernel sources, and the seed. The CPU baseline runs the oracle on a pool of host
+threads and reports the GPU output's error on the heads it computed.
+
 Other modes:
     --no-cpu-baseline        skip the oracle timing
     --copy-calibration MIB   run a plain device copy of MIB MiB (to calibrate HBM byte counters)
@@ -116,51 +124,126 @@ def traffic_from_profiles(w):
         return None
 
 
-def cpu_baseline(w, inp, budget_s: float = 15.0) -> dict:
-    """Time the fp64 oracle on whole (batch, head) pairs of the same inputs until the budget is spent."""
+def counters_from_profiles(w):
+    """Achieved clock and unit utilisation of the kernel from the committed
+    counter summary profiles/<kernel>_<workload>_sq.txt (one rocprofv3 --pmc
+    pass of GRBM_GUI_ACTIVE and SQ counters), or None when it is missing or was
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name(w)}_{w.name}_sq.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            key, sep, val = line.partition(":")
+            if sep and not key.startswith("#"):
+                rec[key.strip()] = val.strip()
+    if rec.get("kernel_source_sha") != kernel_source_hash(kernel_name(w)):
+        return None
+    out = {}
+    for key in ("achieved_clock_mhz", "mfma_busy_pct", "valu_busy_pct", "lds_active_pct", "lds_bank_conflict_pct",
+                "mfma_valu_coexec_pct"):
+        try:
+            out[key] = float(rec[key])
+        except (KeyError, ValueError):
+            out[key] = None
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
+
+
+def cpu_baseline(w, inp, budget_s: float = 15.0, gpu_out=None, gpu_lse=None) -> dict:
+    """Time the fp64 oracle on whole (batch, head) pairs of the same inputs, on a
+    pool of host threads (one (b, h) pair per task, one BLAS thread each), until
+    the budget is spent. When the GPU's output is given, also report its max and
+    mean |GPU - oracle| over the pairs the oracle computed."""
+    import threading
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
     import oracle
     from oracle import e4m3
 
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:
-        threads = 1
+    workers = max(1, min(16, os.cpu_count() or 1))
     G = w.Hq // w.Hkv
 
     def as64(t, name):
         if w.dtype == "fp8":
-            return e4m3.decode(t.numpy()) * inp["descale_" + name]
+            return e4m3.dequantise(t.numpy(), inp["descale_" + name])
         return t.to(torch.float64).numpy()
 
-    heads = 0
+    o_cpu = gpu_out.to(torch.float64).cpu() if gpu_out is not None else None
+    l_cpu = gpu_lse.to(torch.float64).cpu() if gpu_lse is not None else None
+    lock = threading.Lock()
+    done = {"heads": 0, "t_last": 0.0, "err_max": 0.0, "err_sum": 0.0, "err_n": 0, "lse_max": 0.0}
     t0 = time.perf_counter()
-    elapsed = 0.0
-    for b in range(w.B):
-        for h in range(w.Hq):
-            q = as64(inp["q"][b, h], "q")[None, None]
-            k = as64(inp["k"][b, h // G], "k")[None, None]
-            v = as64(inp["v"][b, h // G], "v")[None, None]
-            if w.path == "bwd":
-                oracle.attention_backward(q, k, v, inp["dout"][b, h].to(torch.float64).numpy()[None, None],
-                                          w.scale, w.causal)
-            else:
-                oracle.attention(q, k, v, w.scale, w.causal)
-            heads += 1
-            elapsed = time.perf_counter() - t0
-            if elapsed >= budget_s:
-                break
-        if elapsed >= budget_s:
-            break
+
+    def one(b, h):
+        if time.perf_counter() - t0 >= budget_s:
+            return
+        q = as64(inp["q"][b, h], "q")[None, None]
+        k = as64(inp["k"][b, h // G], "k")[None, None]
+        v = as64(inp["v"][b, h // G], "v")[None, None]
+        if w.path == "bwd":
+            oracle.attention_backward(q, k, v, inp["dout"][b, h].to(torch.float64).numpy()[None, None],
+                                      w.scale, w.causal)
+            o_ref = lse_ref = None
+        else:
+            o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+        t = time.perf_counter() - t0
+        with lock:
+            done["heads"] += 1
+            done["t_last"] = max(done["t_last"], t)
+            if o_ref is not None and o_cpu is not None:
+                err = np.abs(o_cpu[b, h].numpy() - o_ref[0, 0])
+                done["err_max"] = max(done["err_max"], float(err.max()))
+                done["err_sum"] += float(err.sum())
+                done["err_n"] += err.size
+                if l_cpu is not None:
+                    done["lse_max"] = max(done["lse_max"], float(np.abs(l_cpu[b, h].numpy() - lse_ref[0, 0]).max()))
+
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits(1)
+    except Exception:
+        limit = None
+    try:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda bh: one(*bh), [(b, h) for b in range(w.B) for h in range(w.Hq)]))
+    finally:
+        if limit is not None:
+            limit.unregister() if hasattr(limit, "unregister") else limit.__exit__(None, None, None)
+    elapsed = max(done["t_last"], 1e-9)
+    heads = done["heads"]
     flop_per_head = w.flops() / (w.B * w.Hq)
-    value = flop_per_head * heads / elapsed / 1e12
-    return {"value": value, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same workload, full fp64 oracle, "
-                      f"{elapsed:.1f} s wall; FLOP counted causal-adjusted like the GPU value",
-            "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+    rec = {"value": flop_per_head * heads / elapsed / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same workload, full fp64 oracle, "
+                     f"{workers} host threads (one pair per task, one BLAS thread each), {elapsed:.1f} s wall; "
+                     "FLOP counted causal-adjusted like the GPU value",
+           "cpu": platform.processor() or platform.machine(), "os_cpu_count": os.cpu_count()}
+    if done["err_n"]:
+        rec["gpu_vs_oracle"] = {"heads": heads, "max_abs_err_o": done["err_max"],
+                                "mean_abs_err_o": done["err_sum"] / done["err_n"],
+                                "max_abs_err_lse": done["lse_max"] if l_cpu is not None else None}
+    return rec
+
+
+def hip_clock_rate_mhz():
+    """Peak clock the HIP runtime reports for device 0 (hipDeviceAttributeClockRate, kHz)."""
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:  # 5 = hipDeviceAttributeClockRate
+            return val.value / 1000.0
+    except Exception:
+        pass
+    return None
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(math.ceil(q * len(xs))) - 1))]
 
 
 def copy_calibration(mib: int) -> None:
@@ -249,6 +332,10 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--eager", action="store_true")
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="after --warmup calls, keep launching for this long before timing")
+    ap.add_argument("--eager-launches", type=int, default=50,
+                    help="single launches timed after the graph replay (median / min / p90)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -308,7 +395,13 @@ def main() -> int:
         else:
             sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, out=out, lse_out=lse)
 
-    log(f"[bench] warmup {args.warmup}")
+    props = torch.cuda.get_device_properties(0)
+
+    # Warm-up: --warmup calls; then (for forward steps) the graph of K launches
+    # is captured and checked; then more launches until --warm-seconds have
+    # passed, right before the timed region, so it starts at the clocks a
+    # sustained run holds.
+    log(f"[bench] warmup {args.warmup} calls + {args.warm_seconds:.1f} s of launches")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -335,8 +428,32 @@ def main() -> int:
         if not torch.equal(out, eager_out):
             raise RuntimeError("the graph replay's output differs from the eager call's")
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    t_w0 = time.perf_counter()
+    chunk, n_warm = 1, args.warmup
+    while time.perf_counter() - t_w0 < args.warm_seconds:
+        t_c = time.perf_counter()
+        for _ in range(chunk):
+            if use_graph:
+                graph.replay()
+            else:
+                step()
+        torch.cuda.synchronize()
+        n_warm += chunk * (args.steps if use_graph else 1)
+        if time.perf_counter() - t_c < 0.02:
+            chunk *= 2
+
+    def eager_launches(n):
+        """n launches, each between two events on the launch stream; sorted durations in ms."""
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for i in range(n):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+
     log(f"[bench] timing {args.steps} steps" + (" (one graph replay)" if use_graph else ""))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -344,6 +461,8 @@ def main() -> int:
     if use_graph:
         graph.replay()
     else:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         for i in range(args.steps):
             starts[i].record(stream)
             step()
@@ -356,15 +475,19 @@ def main() -> int:
     if use_graph:
         per_launch = [region_ms / args.steps]
     else:
-        per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+        per_launch = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     avg_launch_ms = sum(per_launch) / len(per_launch)
     ms_per_step = region_ms / args.steps
+
+    # Distribution of single launches (events around each call), beside the graph value.
+    dist = eager_launches(args.eager_launches) if use_graph else per_launch
+
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, launch avg {avg_launch_ms * 1e3:.1f} us "
-        f"(median {per_launch[len(per_launch) // 2] * 1e3:.1f}, min {per_launch[0] * 1e3:.1f}), "
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, launch avg {avg_launch_ms * 1e3:.1f} us; single launches: "
+        f"median {percentile(dist, 0.5) * 1e3:.1f}, min {dist[0] * 1e3:.1f}, p90 {percentile(dist, 0.9) * 1e3:.1f} us; "
         f"host wall {t_wall / args.steps * 1e3:.1f} us/step")
 
     # The roofline that bounds the workload: below the ridge point (peak FLOP/s
@@ -391,7 +514,8 @@ def main() -> int:
                 + (", N(0,1) dO; O and lse from the forward kernel" if w.path == "bwd" else ""),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk, "d": w.d,
                    "causal": w.causal, "lse": w.want_lse, "in_dtype": w.dtype, "path": w.path,
-                   "out_dtype": "f32" if w.dtype == "f32" else "bf16", "parallelism": "single GPU"},
+                   "out_dtype": "f32" if w.dtype == "f32" else "bf16", "seed": w.seed,
+                   "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "tokens_per_s": round(w.B * w.Sq / (ms_per_step * 1e-3), 1),
         "hbm_gbs_algorithmic": round(w.hbm_bytes() / (ms_per_step * 1e-3) / 1e9, 1),
@@ -407,6 +531,13 @@ def main() -> int:
             "algorithmic_bytes_per_launch": w.hbm_bytes(),
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
         },
+        "single_launch_us": {"n": len(dist), "median": round(percentile(dist, 0.5) * 1e3, 2),
+                             "min": round(dist[0] * 1e3, 2), "p90": round(percentile(dist, 0.9) * 1e3, 2),
+                             "method": "events around each of n eager calls after the timed region"},
+        "device": {"name": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+                   "cu_count": props.multi_processor_count, "peak_clock_mhz": hip_clock_rate_mhz(),
+                   "warmup_launches": n_warm},
+        "counters": counters_from_profiles(w),
         "cpu_baseline": None,
         "kernel_source_sha": kernel_source_hash(kernel_name(w)),
         "timing": "one HIP graph of the K launches, replayed once" if use_graph else "events around each of K launches",
@@ -414,7 +545,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on a bounded sample ({args.cpu_budget:.0f} s budget)")
-        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, gpu_out=out if w.path != "bwd" else None,
+                                           gpu_lse=lse if w.path != "bwd" else None)
     print(json.dumps(rec), flush=True)
     return 0
 

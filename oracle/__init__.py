@@ -15,13 +15,16 @@ V, causal last row equals the unmasked one, GQA equals MHA on repeated KV
 heads, key shift, affine V, key permutation), brute force at 50 digits on
 tiny inputs, torch's own fp64 CPU attention routine as an independent
 library special case, hand-derived fixtures under tests/golden/, and the
-E4M3 decoder checked exhaustively against torch.float8_e4m3fn.
+E4M3 decoder checked exhaustively against torch.float8_e4m3fn; the
+dequantiser (code times per-tensor descale) pinned by the amax element
+mapping back to the amax and every element of a quantised tensor
+round-tripping within half an E4M3 step.
 
 The gradients (backward.py) are pinned by central finite differences of the
 forward oracle, closed forms (zero query, equal value rows, a single key), the
 GQA head-sum identity and torch's fp64 autograd of its CPU attention.
 """
 
-from .attention import attention, attention_rows, attention_sampled, dequantise, head_of  # noqa: F401
+from .attention import attention, attention_rows, attention_sampled  # noqa: F401
 from .backward import attention_backward  # noqa: F401
 from . import e4m3  # noqa: F401

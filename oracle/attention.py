@@ -38,7 +38,7 @@ computing them in blocks changes no value.
 
 from __future__ import annotations
 
-from typing import Iterable, Optional, Tuple
+from typing import Iterable, Tuple
 
 import numpy as np
 
@@ -120,15 +120,3 @@ def attention_sampled(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
         o, lse = attention_rows(q[b, h, rows], k[b, h // G], v[b, h // G], scale, rows, causal, Sk - Sq)
         out.append((b, h, rows, o, lse))
     return out
-
-
-def head_of(h: int, Hq: int, Hkv: int) -> int:
-    """KV head read by query head h: consecutive groups of Hq // Hkv query heads share one."""
-    return h // (Hq // Hkv)
-
-
-def dequantise(codes_f64: np.ndarray, descale: Optional[float]) -> np.ndarray:
-    """Scaled fp8 values: each decoded code times the per-tensor descale, in fp64 (exact)."""
-    if descale is None:
-        return codes_f64
-    return codes_f64 * float(descale)

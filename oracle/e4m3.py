@@ -13,9 +13,16 @@ Decoding, from the format's definition:
   exponent field e == 0: subnormal  (-1)^s * (m / 8) * 2^(1 - 7)
   0 < e and not NaN:      normal     (-1)^s * (1 + m / 8) * 2^(e - 7)
   e == 15 and m == 7:     NaN
+
+The inputs of the fp8 path are codes plus one fp32 descale per tensor (the
+codelab's section 10 scales each tensor by a factor derived from its amax):
+the real value of a code is its decoded value times the descale, which
+``dequantise`` forms in fp64 (exact: a 4-bit significand times a 24-bit one).
 """
 
 from __future__ import annotations
+
+from typing import Optional
 
 import numpy as np
 
@@ -44,3 +51,13 @@ def decode(codes: np.ndarray) -> np.ndarray:
     if codes.dtype != np.uint8:
         raise TypeError("e4m3 codes must be uint8")
     return _TABLE[codes]
+
+
+def dequantise(codes: np.ndarray, descale: Optional[float]) -> np.ndarray:
+    """Real values of uint8 E4M3fn codes under a per-tensor descale, fp64 (exact).
+
+    ``descale=None`` means unscaled codes (a descale of 1)."""
+    values = decode(codes)
+    if descale is None:
+        return values
+    return values * float(descale)

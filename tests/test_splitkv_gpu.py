@@ -3,7 +3,7 @@
 Decode shapes: one or a few queries against many keys, the query heads of a
 GQA/MQA group packed together, keys cut into chunks merged through their
 log-sum-exps. Every case is compared element by element with the full oracle
-at the bf16 tolerances of the fused forward (O 2e-2, lse 4e-3); the key counts
+at the bf16 tolerances of the fused forward (O 2e-2, lse 1e-4); the key counts
 span one block, block edges (31/32/33), ragged tails and several chunks.
 """
 
@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import sdpa_inputs
-from parity_util import check_full, log, to_device
+from parity_util import TOL_LSE, TOL_O, check_full, log, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -66,8 +66,9 @@ def test_agrees_with_fused_forward(gpu):
     _, inp, dev, o, lse = _run(w)
     o2, lse2 = sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=True, scale=w.scale, want_lse=True)
     torch.cuda.synchronize()
-    assert (o.float() - o2.float()).abs().max().item() <= 2e-2
-    assert (lse - lse2).abs().max().item() <= 4e-3
+    # both are within the oracle tolerances, so they agree within twice those
+    assert (o.float() - o2.float()).abs().max().item() <= 2 * TOL_O["bf16"]
+    assert (lse - lse2).abs().max().item() <= 2 * TOL_LSE["bf16"]
 
 
 def test_decode_at_serving_size(gpu):
