@@ -68,10 +68,11 @@ enum {
   ATTN_ERR_DTYPE = -6,         /* dtype is not an attn_dtype_t value                    */
   ATTN_ERR_SCALE = -7,         /* scale or a descale is not finite and > 0              */
   ATTN_ERR_ALIGN = -8,         /* a base pointer is not 16-byte aligned                 */
-  ATTN_ERR_LAUNCH = -9,        /* the HIP runtime rejected the kernel launch            */
+  ATTN_ERR_LAUNCH = -9,        /* the HIP runtime rejected the launch or a device query */
   ATTN_ERR_WORKSPACE = -10,    /* split-KV workspace missing, misaligned or too small   */
   ATTN_ERR_SPLITS = -11,       /* num_splits outside [0, 128]                           */
-  ATTN_ERR_STRIDE = -12        /* attn_fwd_strided: unusable strides (see there)        */
+  ATTN_ERR_STRIDE = -12,       /* attn_fwd_strided: unusable strides (see there)        */
+  ATTN_ERR_SCRATCH = -13       /* attn_fwd_splitkv_noalloc: needs more than ATTN_SCRATCH_BYTES */
 };
 
 /*
@@ -223,6 +224,34 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int Hq, int Hkv, int Sq, int Sk, int d,
              float scale, int causal, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments (minus workspace), same kernels, bit-identical results.
+ *
+ * The key chunks' partial outputs and log-sum-exps go to a static device
+ * array inside the library, ATTN_SCRATCH_BYTES (16 MiB) per GPU, held by each
+ * GPU the library runs on until the process ends. Nothing is allocated: no
+ * hipMalloc, no hipFree, no allocating library call. The array's device
+ * address is looked up on the first call on each device (the current device;
+ * `stream` must belong to it). The chunk kernel writes every entry the merge
+ * kernel reads, so no call depends on what an earlier call left there.
+ *
+ * Every call on one GPU shares that GPU's array: two calls whose work can
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race on it and may return wrong results. Calls on one stream are ordered
+ * and safe.
+ *
+ * Returns ATTN_OK, ATTN_ERR_SCRATCH when attn_fwd_splitkv_plan reports more
+ * than ATTN_SCRATCH_BYTES of workspace for these sizes and num_splits
+ * (nothing is enqueued), or the other statuses of attn_fwd_splitkv.
+ */
+#define ATTN_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                             float scale, int causal, int dtype, int num_splits, hipStream_t stream);
 
 /* attn_bwd_workspace_size -- host-only: the workspace bytes attn_bwd needs
  * for these sizes (*workspace_bytes, may be NULL). Returns ATTN_OK or the

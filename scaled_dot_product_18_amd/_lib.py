@@ -30,7 +30,11 @@ STATUS = {
     -10: "ATTN_ERR_WORKSPACE",
     -11: "ATTN_ERR_SPLITS",
     -12: "ATTN_ERR_STRIDE",
+    -13: "ATTN_ERR_SCRATCH",
 }
+
+# Bytes of the library's static scratch used by attn_fwd_splitkv_noalloc (ATTN_SCRATCH_BYTES).
+SCRATCH_BYTES = 16 << 20
 
 _lock = threading.Lock()
 _lib = None
@@ -62,6 +66,8 @@ def load() -> ctypes.CDLL:
         sz = ctypes.c_size_t
         lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
         lib.attn_fwd_splitkv.restype = i
+        lib.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+        lib.attn_fwd_splitkv_noalloc.restype = i
         lib.attn_fwd_splitkv_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(sz)]
         lib.attn_fwd_splitkv_plan.restype = i
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -103,6 +109,13 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtyp
     """Raw call with integer pointers; returns the status code."""
     return load().attn_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dtype, num_splits,
                                    ws, ws_bytes, stream)
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, num_splits,
+                             stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), dtype,
+                                           num_splits, stream)
 
 
 def attn_fwd_splitkv_plan(B, Hq, Hkv, Sq, Sk, d, num_splits):

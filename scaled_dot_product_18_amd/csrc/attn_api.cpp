@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn.h"
 #include "kernel_common.h"
 #include "launch.h"
@@ -195,6 +197,68 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
+// Scratch of attn_fwd_splitkv_noalloc: the key chunks' partial outputs and
+// log-sum-exps, in a static device array instead of caller memory. Every GPU
+// the library runs on holds its own copy until the process ends; in host code
+// `scratch` names a host-side stand-in, so kernels receive the device address
+// that hipGetSymbolAddress reports, taken once per device with that device
+// current and kept below.
+static __device__ __align__(256) unsigned char scratch[ATTN_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (set up on the first call on
+// that device). Returns ATTN_OK or ATTN_ERR_LAUNCH when the runtime refuses.
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> guard(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return ATTN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// Shared path of attn_fwd_splitkv (caller workspace) and
+// attn_fwd_splitkv_noalloc (use_scratch: the library's static scratch).
+int splitkv_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Sq,
+                   int Sk, int d, float scale, int causal, int dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, bool use_scratch, hipStream_t stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  st = validate_split_sizes(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
+  const SplitPlan pl = plan_splits(B, Hq, Hkv, Sq, Sk, d, num_splits);
+  if (use_scratch) {
+    if (pl.workspace > ATTN_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    workspace = nullptr;
+    if (pl.workspace > 0) {
+      st = device_scratch(&workspace);
+      if (st != ATTN_OK) return st;
+    }
+  } else if (pl.workspace > 0 &&
+             (workspace == nullptr || !aligned16(workspace) || workspace_bytes < pl.workspace)) {
+    return ATTN_ERR_WORKSPACE;
+  }
+  sdpa18::SplitParams sp;
+  sp.a = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, 128, dense_strides(Hq, Hkv, Sq, Sk, d), 2,
+                     2);
+  const size_t rows = (size_t)B * Hq * Sq;
+  sp.part_o = pl.workspace > 0 ? static_cast<float*>(workspace) : nullptr;
+  sp.part_lse = pl.workspace > 0 ? static_cast<float*>(workspace) + rows * pl.n_splits * (size_t)d : nullptr;
+  sp.n_splits = pl.n_splits;
+  sp.chunk = pl.chunk;
+  sp.n_ctiles = pl.n_ctiles;
+  return launch_status(sdpa18::launch_attn_splitkv_bf16(sp, d, causal != 0, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,25 +300,15 @@ int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                      int Sq, int Sk, int d, float scale, int causal, int dtype, int num_splits, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
-  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
-  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
-  if (st != ATTN_OK) return st;
-  st = validate_split_sizes(B, Hq, Hkv, Sq, Sk, d, num_splits);
-  if (st != ATTN_OK) return st;
-  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
-  const SplitPlan pl = plan_splits(B, Hq, Hkv, Sq, Sk, d, num_splits);
-  if (pl.workspace > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < pl.workspace))
-    return ATTN_ERR_WORKSPACE;
-  sdpa18::SplitParams sp;
-  sp.a = make_params(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale, 1.0f, 128, dense_strides(Hq, Hkv, Sq, Sk, d), 2,
-                     2);
-  const size_t rows = (size_t)B * Hq * Sq;
-  sp.part_o = pl.workspace > 0 ? static_cast<float*>(workspace) : nullptr;
-  sp.part_lse = pl.workspace > 0 ? static_cast<float*>(workspace) + rows * pl.n_splits * (size_t)d : nullptr;
-  sp.n_splits = pl.n_splits;
-  sp.chunk = pl.chunk;
-  sp.n_ctiles = pl.n_ctiles;
-  return launch_status(sdpa18::launch_attn_splitkv_bf16(sp, d, causal != 0, stream));
+  return splitkv_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, num_splits, workspace,
+                        workspace_bytes, false, stream);
+}
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                             int Hkv, int Sq, int Sk, int d, float scale, int causal, int dtype, int num_splits,
+                             hipStream_t stream) {
+  return splitkv_common(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, num_splits, nullptr, 0, true,
+                        stream);
 }
 
 int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes) {
@@ -320,11 +374,14 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";
     case ATTN_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
-    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch (or the device query before it)";
     case ATTN_ERR_WORKSPACE: return "workspace is NULL, not 16-byte aligned or smaller than the size query reports";
     case ATTN_ERR_SPLITS: return "num_splits must be in [0, 128]";
     case ATTN_ERR_STRIDE:
       return "a stride is negative, leaves rows overlapping or not 16-byte aligned, or spans 2 GiB within a head";
+    case ATTN_ERR_SCRATCH:
+      return "attn_fwd_splitkv_noalloc: the request needs more than the library's static scratch "
+             "(ATTN_SCRATCH_BYTES = 16 MiB); use fewer splits or attn_fwd_splitkv with a workspace";
     default: return "unknown status";
   }
 }

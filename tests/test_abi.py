@@ -33,8 +33,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _header_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp8",
-                                   "attn_fwd_splitkv", "attn_fwd_splitkv_plan", "attn_fwd_strided", "attn_strerror",
-                                   "attn_version"]
+                                   "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_plan",
+                                   "attn_fwd_strided", "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -127,6 +127,36 @@ def test_splitkv_validation_errors(lib):
     st, n, nbytes = lib.attn_fwd_splitkv_plan(1, 4, 1, 1, 4096, 128, 8)
     assert (st, n) == (0, 8) and nbytes == 4 * 8 * 129 * 4
     assert call(ws_bytes=nbytes - 1) == -10
+
+
+def test_splitkv_noalloc_validation_errors(lib):
+    """The no-allocation variant checks its arguments like attn_fwd_splitkv, and rejects
+    requests whose chunk partials exceed the static scratch (ATTN_SCRATCH_BYTES, 16 MiB)
+    before any HIP call (so these run without a GPU)."""
+    f = lib.load().attn_fwd_splitkv_noalloc
+    ok = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=1, Sq=1, Sk=4096, d=128, scale=0.1, causal=0,
+              dtype=1, ns=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"],
+                 a["scale"], a["causal"], a["dtype"], a["ns"], None)
+
+    assert call(dtype=0) == -6 and call(dtype=2) == -6
+    assert call(o=None) == -1
+    assert call(Sq=0) == -2
+    assert call(Hkv=3) == -3
+    assert call(d=96) == -4
+    assert call(causal=1, Sq=4097) == -5
+    assert call(scale=0.0) == -7
+    assert call(q=P + 4) == -8
+    assert call(ns=-1) == -11 and call(ns=129) == -11
+    # B*Hq*Sq*splits*(d+1)*4 bytes: 64*32*8*128*129*4 > 16 MiB; the plan agrees
+    big = dict(B=64, Hq=32, Hkv=8, Sq=8, Sk=32768, ns=128)
+    st, n, nbytes = lib.attn_fwd_splitkv_plan(64, 32, 8, 8, 32768, 128, 128)
+    assert st == 0 and nbytes > 16 << 20
+    assert call(**big) == -13
+    assert "16 MiB" in lib.strerror(-13)
 
 
 @pytest.mark.parametrize("sizes,ns", [((4, 32, 8, 1, 4096, 128), 0), ((4, 32, 32, 1, 4096, 128), 0),
