@@ -264,8 +264,12 @@ def sweep_shapes():
     (section 3); section 8 sweeps the sequence length over 64..1024 and the batch
     over 1..16 at T=256, unmasked, in fp32 and bf16; the TransformerEngine cell
     sweeps causal bf16 over T=128..2048; the FP8 cell runs causal attention at
-    T=2048. Seeds follow the cells' key numbers (sl, bs + 100, sl + 1000, 9000).
-    Returns (sweep name, Workload) pairs in the library's [B, H, S, d] layout."""
+    T=2048. Its closing next steps try head dimensions 32, 64 and 128 (here in
+    fp32, bf16 and fp8 at T=1024, unmasked and causal) and re-run the MHA / GQA /
+    MQA cell (8 query heads against 8, 2 and 1 KV heads; section 9's cell is
+    B=2, T=64) at longer sequences. Seeds follow the cells' key numbers (sl,
+    bs + 100, sl + 1000, 9000, 42). Returns (sweep name, Workload) pairs in the
+    library's [B, H, S, d] layout."""
     import sdpa_inputs
     B, N, H = 4, 8, 64
     out = []
@@ -280,12 +284,24 @@ def sweep_shapes():
         out.append(("causal_bf16", sdpa_inputs.custom(B, N, N, sl, sl, H, "bf16", True, seed=sl + 1000,
                                                       name=f"causal_bf16_b{B}_t{sl}")))
     out.append(("fp8", sdpa_inputs.custom(B, N, N, 2048, 2048, H, "fp8", True, seed=9000, name=f"fp8_causal_b{B}_t2048")))
+    for dtype in ("f32", "bf16", "fp8"):
+        for hd in (32, 64, 128):
+            for causal in (False, True):
+                out.append(("head_dim", sdpa_inputs.custom(B, N, N, 1024, 1024, hd, dtype, causal, seed=1024,
+                                                           name=f"head_dim_{dtype}_d{hd}_t1024_{'c' if causal else 'n'}")))
+    for sl in (1024, 4096):
+        for hkv in (8, 2, 1):
+            out.append(("mha_gqa_mqa", sdpa_inputs.custom(2, N, hkv, sl, sl, H, "bf16", True, seed=42,
+                                                          name=f"kv_heads_{hkv}_bf16_b2_t{sl}")))
     return out
 
 
 def run_sweep(warmup: int = 2, repeats: int = 20) -> int:
     """Time every sweep shape like the codelab's helper (warm-up calls, then the
-    median of the timed calls), with HIP events on the launch stream."""
+    median of the timed calls, each with HIP events on the launch stream around
+    the Python call, so launch overhead is included), and also as one HIP graph
+    of the same number of launches (the kernel time per launch, which the
+    roofline fraction uses)."""
     import torch
     import sdpa_inputs
     import scaled_dot_product_18_amd as sdpa
@@ -294,13 +310,15 @@ def run_sweep(warmup: int = 2, repeats: int = 20) -> int:
     for sweep, w in sweep_shapes():
         inp = sdpa_inputs.make_inputs(w)
         dev = {n: inp[n].cuda() for n in ("q", "k", "v")}
+        out = torch.empty((w.B, w.Hq, w.Sq, w.d), dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
+                          device="cuda")
 
         def call():
             if w.dtype == "fp8":
                 sdpa.fwd_fp8(dev["q"], dev["k"], dev["v"], inp["descale_q"], inp["descale_k"], inp["descale_v"],
-                             causal=w.causal, scale=w.scale)
+                             causal=w.causal, scale=w.scale, out=out)
             else:
-                sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+                sdpa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale, out=out)
 
         for _ in range(warmup):
             call()
@@ -314,10 +332,27 @@ def run_sweep(warmup: int = 2, repeats: int = 20) -> int:
             b.synchronize()
             times.append(a.elapsed_time(b))
         med = sorted(times)[len(times) // 2]
-        print(json.dumps({"sweep": sweep, "workload": w.name, "B": w.B, "T": w.Sq, "N": w.Hq, "H": w.d,
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(repeats):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        b.synchronize()
+        per_launch = a.elapsed_time(b) / repeats
+        peak = PEAK_TFLOPS[w.dtype]
+        print(json.dumps({"sweep": sweep, "workload": w.name, "B": w.B, "T": w.Sq, "N": w.Hq, "K": w.Hkv, "H": w.d,
                           "dtype": w.dtype, "causal": w.causal, "ms_median": round(med, 5),
                           "tflops": round(w.flops() / (med * 1e-3) / 1e12, 3),
-                          "tokens_per_s": round(w.B * w.Sq / (med * 1e-3), 1)}), flush=True)
+                          "tokens_per_s": round(w.B * w.Sq / (med * 1e-3), 1),
+                          "graph_us_per_launch": round(per_launch * 1e3, 2),
+                          "graph_tflops": round(w.flops() / (per_launch * 1e-3) / 1e12, 2),
+                          "graph_pct_of_peak": round(100 * w.flops() / (per_launch * 1e-3) / 1e12 / peak, 2),
+                          "kernel": kernel_name(w)}), flush=True)
     return 0
 
 

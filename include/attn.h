@@ -63,7 +63,7 @@ enum {
   ATTN_ERR_NULL = -1,          /* a required pointer is NULL (q, k, v, o; see attn_bwd) */
   ATTN_ERR_SHAPE = -2,         /* a size is < 1, or the problem exceeds 32-bit indexing */
   ATTN_ERR_HEADS = -3,         /* Hq is not a multiple of Hkv                           */
-  ATTN_ERR_HEADDIM = -4,       /* d is not 64 or 128                                    */
+  ATTN_ERR_HEADDIM = -4,       /* d not in {32, 64, 128} ({64, 128}: split-KV, backward) */
   ATTN_ERR_CAUSAL_SHAPE = -5,  /* causal requested with Sq > Sk                         */
   ATTN_ERR_DTYPE = -6,         /* dtype is not an attn_dtype_t value                    */
   ATTN_ERR_SCALE = -7,         /* scale or a descale is not finite and > 0              */
@@ -81,7 +81,8 @@ enum {
  *   q, k, v  device inputs of element type `dtype`, layouts above.
  *   o        device output: float32 for ATTN_F32, bfloat16 otherwise.
  *   lse      device float32 [B, Hq, Sq] or NULL to skip the statistic.
- *   B, Hq, Hkv, Sq, Sk, d   sizes; Hq % Hkv == 0; d in {64, 128};
+ *   B, Hq, Hkv, Sq, Sk, d   sizes; Hq % Hkv == 0; d in {32, 64, 128} (the
+ *            codelab's closing next steps try head dimensions 32, 64 and 128);
  *            causal requires Sq <= Sk.
  *   scale    multiplier of the dot products, finite and > 0 (the pages use
  *            1/sqrt(d)).
@@ -152,7 +153,8 @@ int attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float
  * softmax in the article's section 3). Results agree with attn_fwd up to
  * rounding.
  *
- *   q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream  as attn_fwd.
+ *   q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, scale, causal, stream  as attn_fwd,
+ *                except d in {64, 128}.
  *   dtype        ATTN_BF16 only (ATTN_ERR_DTYPE otherwise).
  *   num_splits   0 = the library's choice (enough chunks to fill the GPU, at
  *                least 256 keys each), else at most 128 chunks; a chunk holds
@@ -203,6 +205,7 @@ int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num
  *   dq        output, layout of q; dk, dv outputs, layout of k / v. Every
  *             element is written (a KV head's gradient is the sum over its
  *             query heads, computed without atomics);
+ *   d         64 or 128;
  *   dtype     ATTN_BF16 only: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse;
  *   workspace device memory owned by the caller, 16-byte aligned, at least
  *             attn_bwd_workspace_size bytes: 2*B*Hq*Sq floats (the per-row

@@ -32,7 +32,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
       tiles * (int64_t)B * (int64_t)Hq >= INT32_MAX)
     return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if (causal && Sq > Sk) return ATTN_ERR_CAUSAL_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
   return ATTN_OK;
@@ -327,6 +327,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_ERR_NULL;
   int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
   if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if ((int64_t)((Sk + 127) / 128) * B * Hkv >= INT32_MAX) return ATTN_ERR_SHAPE;
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
   if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
@@ -369,7 +370,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_NULL: return "a required pointer (q, k, v, o; for attn_bwd also dout, lse, dq, dk, dv) is null";
     case ATTN_ERR_SHAPE: return "a size is < 1 or the problem exceeds 32-bit indexing";
     case ATTN_ERR_HEADS: return "Hq is not a multiple of Hkv";
-    case ATTN_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_HEADDIM:
+      return "head dimension d must be 32, 64 or 128 (64 or 128 for the split-KV and backward entry points)";
     case ATTN_ERR_CAUSAL_SHAPE: return "causal masking requires Sq <= Sk";
     case ATTN_ERR_DTYPE: return "unknown dtype";
     case ATTN_ERR_SCALE: return "scale and descales must be finite and > 0";

@@ -10,8 +10,8 @@
 // its section 7 and the shared KV heads of its section 9.
 //
 // Layout of the work on CDNA4:
-//  * this four-wave kernel serves head dimension 64 (the eight-wave ping-pong
-//    kernel in attn_fwd_bf16_pp.hip serves 128);
+//  * this four-wave kernel serves head dimensions 32 and 64 (the eight-wave
+//    ping-pong kernel in attn_fwd_bf16_pp.hip serves 128);
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //    wave w owns rows [32w, 32w+32) and keeps their Q fragment in VGPRs;
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16,
@@ -65,16 +65,19 @@ struct Bf16Cfg {
 
 // Chunk swizzle of K rows: lanes 0..15 of an operand read hit 16 different rows
 // at one logical chunk; XOR with a row-dependent value spreads them over all banks.
+// At d = 32 a row is 64 bytes (4 chunks): rows 4 apart share banks, so the
+// chunk is XORed with bits 2-3 of the row.
 template <int D>
 __device__ __forceinline__ int k_swizzle(int row) {
-  return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+  return D == 128 ? (row & 15) : D == 64 ? ((row & 7) ^ ((row >> 3) & 1)) : ((row >> 2) & 3);
 }
 // Chunk swizzle of V rows: a 16-lane transposing read touches 4 consecutive rows
 // at 32 consecutive bytes; the XOR values {0,6,10,12} (d=128) / {0,2,4,6} (d=64)
-// place the 4 rows on disjoint banks for both 32- and 64-bank LDS.
+// place the 4 rows on disjoint banks for both 32- and 64-bank LDS. At d = 32
+// four consecutive 64-byte rows already fall on disjoint banks.
 template <int D>
 __device__ __forceinline__ int v_swizzle(int row) {
-  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
+  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : D == 64 ? ((0x6420 >> (4 * (row & 3))) & 15) : 0;
 }
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: keep the stale max unless exceeded by 2^8
@@ -335,8 +338,9 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 int bf16_block_m(int d) { return d == 128 ? bf16_pp_block_m() : Bf16Cfg<64>::BM; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream) {
-  // d = 128: the eight-wave ping-pong kernel (attn_fwd_bf16_pp.hip); d = 64 here.
+  // d = 128: the eight-wave ping-pong kernel (attn_fwd_bf16_pp.hip); d = 32 and 64 here.
   if (d == 128) return launch_attn_bf16_pp(p, causal, stream);
+  if (d == 32) return causal ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
   return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }
 

@@ -386,6 +386,7 @@ int f32_block_m() { return 128; }
 
 hipError_t launch_attn_f32(const AttnParams& p, int d, bool causal, hipStream_t stream) {
   if (d == 128) return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+  if (d == 32) return causal ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
   return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }
 

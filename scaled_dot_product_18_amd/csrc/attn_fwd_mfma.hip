@@ -1,6 +1,8 @@
 // Fused scaled dot-product attention forward for gfx950 on fp8-e4m3fn inputs
-// at head dimension 64 (fp8 MFMA for Q.K^T, bf16 MFMA for P.V with V widened
-// exactly); head dimension 128 runs the ping-pong kernel of attn_fwd_fp8_pp.hip.
+// at head dimensions 32 and 64 (fp8 MFMA for Q.K^T, bf16 MFMA for P.V with V
+// widened exactly); head dimension 128 runs the ping-pong kernel of
+// attn_fwd_fp8_pp.hip. The fp8 MFMA has a K depth of 64: at d = 32 the upper
+// half-wave supplies zero operands, so each score is still one instruction.
 // The template also has a bf16-input form (FP8 = false), which nothing
 // launches.
 //
@@ -36,7 +38,7 @@ namespace sdpa18 {
 template <int D, bool FP8>
 struct MfmaCfg {
   static constexpr int BM = 128;                    // query rows per workgroup
-  static constexpr int BN = 8192 / D;               // keys per tile: 64 (d=128), 128 (d=64)
+  static constexpr int BN = D == 32 ? 128 : 8192 / D;  // keys per tile: 64 (d=128), 128 (d=64, d=32)
   static constexpr int ES = FP8 ? 1 : 2;            // bytes per Q/K/V input element
   static constexpr int KRB = D * ES;                // bytes per K row in LDS
   static constexpr int KCH = KRB / 16;              // 16-byte chunks per K row
@@ -49,11 +51,12 @@ struct MfmaCfg {
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int KC = BN / 16;                // 16-key chunks (K dim of P.V)
   static constexpr int DB = D / 32;                 // 32-wide output blocks
-  static constexpr int QK_STEPS = FP8 ? D / 64 : D / 16;  // MFMAs per 32x32 score block
+  static constexpr int QK_STEPS = FP8 ? (D + 63) / 64 : D / 16;  // MFMAs per 32x32 score block
   static constexpr int QREGS = FP8 ? 2 * QK_STEPS : QK_STEPS;  // 16-byte Q pieces per lane
   static constexpr int VU = BN / 4;                 // 4-key units per V^T row
+  static constexpr int VTHREADS = VU * D / 8;       // threads that stage V (4 keys x 8 dims each)
   static_assert(KPASS >= 1 && KROWS_PER_PASS * KPASS == BN, "K staging must tile the key block");
-  static_assert((256 / VU) * 8 == D, "V staging: 256 threads x (4 keys x 8 dims) must tile BN x D");
+  static_assert(VTHREADS <= 256 && VTHREADS * 32 == BN * D, "V staging: 4 keys x 8 dims per thread tile BN x D");
 };
 
 // E8M0 scale byte 127 = 2^0: the scaled fp8 MFMA with unit scales.
@@ -100,7 +103,9 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 #pragma unroll
   for (int s = 0; s < C::QREGS; ++s) {
     const int byte = FP8 ? (64 * (s >> 1) + 32 * g + 16 * (s & 1)) : (32 * s + 16 * g);
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + byte) : u32x4{0, 0, 0, 0};
+    // fp8 at d = 32: the upper half-wave holds the zero half of the 64-deep operand
+    const bool in_row = !(FP8 && D == 32) || g == 0;
+    qf[s] = (qi < p.Sq && in_row) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + byte) : u32x4{0, 0, 0, 0};
   }
 
   // ---- staging assignment --------------------------------------------------
@@ -122,7 +127,9 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kr = kv0 + 4 * vu + t;
-      if (FP8) {
+      if (C::VTHREADS < 256 && tid >= C::VTHREADS) {
+        vreg[t] = u32x4{0, 0, 0, 0};
+      } else if (FP8) {
         u32x2 x = (kr < p.Sk) ? *(const u32x2*)(vbase + (size_t)kr * p.v_ss + vd0) : u32x2{0, 0};
         vreg[t] = u32x4{x[0], x[1], 0, 0};
       } else {
@@ -141,6 +148,7 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
       *(u32x4*)(kl + r * C::KRB + 16 * phys) = kreg[t];
     }
     // V tile -> V^T: row = dim, 4 consecutive keys per 8-byte unit.
+    if (C::VTHREADS < 256 && tid >= C::VTHREADS) return;
     uint32_t w[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -209,8 +217,11 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
 #pragma unroll
         for (int st = 0; st < C::QK_STEPS; ++st) {
           if (FP8) {
-            const u32x4 a0 = *(const u32x4*)(krow + 16 * ((4 * st + 2 * g) ^ kswz));
-            const u32x4 a1 = *(const u32x4*)(krow + 16 * ((4 * st + 2 * g + 1) ^ kswz));
+            // d = 32: both half-waves read the row's two chunks; the upper half's copy
+            // meets the zero half of the Q operand, so it adds nothing
+            const int c0 = D == 32 ? 0 : 4 * st + 2 * g;
+            const u32x4 a0 = *(const u32x4*)(krow + 16 * (c0 ^ kswz));
+            const u32x4 a1 = *(const u32x4*)(krow + 16 * ((c0 + 1) ^ kswz));
             const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
             const u32x4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
@@ -333,6 +344,7 @@ int fp8_block_m(int d) { return d == 128 ? fp8_pp_block_m() : 128; }
 
 hipError_t launch_attn_fp8(const AttnParams& p, int d, bool causal, hipStream_t stream) {
   if (d == 128) return launch_attn_fp8_pp(p, causal, stream);
+  if (d == 32) return causal ? launch_one<32, true, true>(p, stream) : launch_one<32, false, true>(p, stream);
   return causal ? launch_one<64, true, true>(p, stream) : launch_one<64, false, true>(p, stream);
 }
 

@@ -73,7 +73,7 @@ def _call(lib, q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=64,
     (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Sq=0), -2), (dict(Sk=-3), -2), (dict(d=0), -2),
     (dict(Sq=1 << 30), -2),
     (dict(Hq=3, Hkv=2), -3),
-    (dict(d=96), -4), (dict(d=256), -4), (dict(d=32), -4),
+    (dict(d=96), -4), (dict(d=256), -4), (dict(d=16), -4), (dict(d=48), -4),
     (dict(causal=1, Sq=9, Sk=8), -5),
     (dict(dtype=3), -6), (dict(dtype=-1), -6),
     (dict(scale=0.0), -7), (dict(scale=-0.5), -7), (dict(scale=float("inf")), -7), (dict(scale=float("nan")), -7),
@@ -116,7 +116,7 @@ def test_splitkv_validation_errors(lib):
     assert call(o=None) == -1
     assert call(Sq=0) == -2
     assert call(Hkv=3) == -3
-    assert call(d=96) == -4
+    assert call(d=96) == -4 and call(d=32) == -4
     assert call(causal=1, Sq=4097) == -5
     assert call(scale=0.0) == -7
     assert call(q=P + 4) == -8
@@ -146,7 +146,7 @@ def test_splitkv_noalloc_validation_errors(lib):
     assert call(o=None) == -1
     assert call(Sq=0) == -2
     assert call(Hkv=3) == -3
-    assert call(d=96) == -4
+    assert call(d=96) == -4 and call(d=32) == -4
     assert call(causal=1, Sq=4097) == -5
     assert call(scale=0.0) == -7
     assert call(q=P + 4) == -8

@@ -47,14 +47,14 @@ def test_vit_b16_bf16_workload(gpu):
 
 # ------------------------------------------------------- tails, heads, causal
 
-@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product(TAIL_S, (64, 128), (False, True), HEADS)))
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product(TAIL_S, (32, 64, 128), (False, True), HEADS)))
 def test_bf16_tails(gpu, S, d, causal, heads):
     Hq, Hkv = heads
     w = sdpa_inputs.custom(1, Hq, Hkv, S, S, d, "bf16", causal, seed=1000 + S)
     _run_full(w)
 
 
-@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (64, 128),
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (32, 64, 128),
                                                                     (False, True), [(4, 4), (4, 2), (4, 1)])))
 def test_f32_tails(gpu, S, d, causal, heads):
     Hq, Hkv = heads
@@ -75,7 +75,7 @@ def test_f32_grid_sizes(gpu, B, H, S, d, causal):
     _run_full(sdpa_inputs.custom(B, H, H, S, S, d, "f32", causal, seed=2500 + S + d, want_lse=True))
 
 
-@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 63, 64, 65, 129, 257], (64, 128),
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 63, 64, 65, 129, 257], (32, 64, 128),
                                                                     (False, True), HEADS)))
 def test_fp8_tails(gpu, S, d, causal, heads):
     Hq, Hkv = heads
@@ -89,8 +89,8 @@ def test_cross_attention_lengths(gpu, dtype, Sq, Sk):
     _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, 128 if dtype != "f32" else 64, dtype, False, seed=Sq * 7 + Sk))
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128), ("fp8", 64),
-                                     ("fp8", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("f32", 64), ("f32", 128), ("bf16", 32), ("bf16", 64),
+                                     ("bf16", 128), ("fp8", 32), ("fp8", 64), ("fp8", 128)])
 @pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 300), (5, 64), (77, 200), (130, 257), (256, 1000), (300, 301)])
 def test_causal_queries_are_the_last_positions(gpu, dtype, d, Sq, Sk):
     """Causal with Sq < Sk: query i sees keys j <= i + (Sk - Sq) (new queries against a longer key
@@ -98,7 +98,7 @@ def test_causal_queries_are_the_last_positions(gpu, dtype, d, Sq, Sk):
     _run_full(sdpa_inputs.custom(2, 4, 2, Sq, Sk, d, dtype, True, seed=5000 + Sq * 3 + Sk, want_lse=True))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_batch_and_heads_mapping(gpu, d):
     """Several batches and GQA groups at once, causal, lse on."""
     for dtype in ("f32", "bf16", "fp8"):
@@ -131,9 +131,9 @@ def test_golden_fixtures_fp32(gpu):
 
 # ----------------------------------------------------------------- properties
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_large_score_offset(gpu, d):
-    """Scores around 1e3: the online softmax stays finite and matches the oracle."""
+    """Scores around 16 d (500 to 2000): the online softmax stays finite and matches the oracle."""
     import scaled_dot_product_18_amd as sdpa
     g = torch.Generator().manual_seed(5)
     S = 150
@@ -145,13 +145,13 @@ def test_large_score_offset(gpu, d):
         o, lse = sdpa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=1.0, want_lse=True)
         torch.cuda.synchronize()
         o_ref, l_ref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), 1.0, causal)
-        assert np.all(l_ref > 900)
+        assert np.all(l_ref > 12 * d)
         assert np.abs(o.double().cpu().numpy() - o_ref).max() <= TOL_O["bf16"]
         # fp32 scores of magnitude ~1e3 carry ~1e-5 relative rounding on top of the lse bound
         assert np.abs(lse.double().cpu().numpy() - l_ref).max() <= TOL_LSE["bf16"] + 1e-5 * np.abs(l_ref).max()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rising_scores_move_the_reference(gpu, d, causal):
     """Scores that grow along the key sequence by ~100 (natural-log units) force the
@@ -200,7 +200,8 @@ def test_deterministic(gpu):
     assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(l1, l2) and torch.equal(l1, l3)
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128), ("fp8", 64), ("fp8", 128)])
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("f32", 64), ("bf16", 32), ("bf16", 64), ("bf16", 128), ("fp8", 32),
+                                     ("fp8", 64), ("fp8", 128)])
 def test_gqa_equals_mha_on_repeated_kv(gpu, dtype, d):
     """GQA/MQA output is bit-identical to MHA on host-repeated K/V heads."""
     for Hkv in (2, 1):
@@ -227,7 +228,7 @@ def test_causal_first_row_is_v0(gpu):
     assert torch.allclose(lse[:, :, 0].cpu().double(), s0, atol=1e-4)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_lse_optional(gpu, d):
     w = sdpa_inputs.custom(1, 4, 4, 100, 100, d, "bf16", False, seed=41)
     dev = to_device(sdpa_inputs.make_inputs(w))
@@ -243,9 +244,10 @@ def test_errors_raise_through_python(gpu):
     kv = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sdpa.AttnError, match="ATTN_ERR_HEADS"):
         sdpa.fwd(x, kv, kv)
-    y = torch.zeros(1, 2, 8, 96, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(sdpa.AttnError, match="ATTN_ERR_HEADDIM"):
-        sdpa.fwd(y, y, y)
+    for bad_d in (16, 48, 96, 256):
+        y = torch.zeros(1, 2, 8, bad_d, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(sdpa.AttnError, match="ATTN_ERR_HEADDIM"):
+            sdpa.fwd(y, y, y)
     z = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
     z9 = torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sdpa.AttnError, match="ATTN_ERR_CAUSAL_SHAPE"):
