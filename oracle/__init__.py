@@ -18,7 +18,8 @@ library special case, hand-derived fixtures under tests/golden/, and the
 E4M3 decoder checked exhaustively against torch.float8_e4m3fn; the
 dequantiser (code times per-tensor descale) pinned by the amax element
 mapping back to the amax and every element of a quantised tensor
-round-tripping within half an E4M3 step.
+round-tripping within half an E4M3 step; likewise the E5M2 decoder of the
+fp8 backward pass's gradients, exhaustively against torch.float8_e5m2.
 
 The gradients (backward.py) are pinned by central finite differences of the
 forward oracle, closed forms (zero query, equal value rows, a single key), the
@@ -28,3 +29,4 @@ GQA head-sum identity and torch's fp64 autograd of its CPU attention.
 from .attention import attention, attention_rows, attention_sampled  # noqa: F401
 from .backward import attention_backward  # noqa: F401
 from . import e4m3  # noqa: F401
+from . import e5m2  # noqa: F401

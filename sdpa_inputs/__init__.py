@@ -36,6 +36,7 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0  # largest finite OCP e4m3fn magnitude
+E5M2_MAX = 57344.0  # largest finite OCP e5m2 magnitude
 
 DTYPES = ("f32", "bf16", "fp8")
 
@@ -138,6 +139,33 @@ def quantise_e4m3(x: torch.Tensor):
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
     descale = float((torch.tensor(1.0, dtype=torch.float32) / s).item())
     return codes.contiguous(), descale
+
+
+def quantise_e5m2(x: torch.Tensor):
+    """Per-tensor amax quantisation of fp32 ``x`` to OCP fp8-e5m2, the gradient
+    format of the codelab's fp8 recipe (section 10).
+
+    scale = 57344 / amax(|x|) in fp32; codes = RNE(x * scale) saturated to
+    +-57344 (never infinity); descale = 1 / scale in fp32. Returns (codes as
+    uint8 tensor, descale as a Python float holding the exact fp32 value).
+    """
+    x = x.to(torch.float32)
+    amax = float(x.abs().max())
+    if not math.isfinite(amax) or amax == 0.0:
+        amax = 1.0
+    s = torch.tensor(E5M2_MAX, dtype=torch.float32) / torch.tensor(amax, dtype=torch.float32)
+    y = torch.clamp(x * s, -E5M2_MAX, E5M2_MAX)
+    codes = y.to(torch.float8_e5m2).view(torch.uint8)
+    descale = float((torch.tensor(1.0, dtype=torch.float32) / s).item())
+    return codes.contiguous(), descale
+
+
+def draw_grad_fp8(w: Workload, seed: Optional[int] = None):
+    """The upstream gradient of draw_grad's stream as fp8-e5m2 codes with a
+    per-tensor descale: (codes uint8 [B, Hq, Sq, d], descale)."""
+    seed = w.seed if seed is None else seed
+    g = _normal(np.random.SeedSequence([seed, 3]), (w.B, w.Hq, w.Sq, w.d))
+    return quantise_e5m2(torch.from_numpy(g))
 
 
 def draw_grad(w: Workload, seed: Optional[int] = None) -> torch.Tensor:

@@ -14,7 +14,10 @@ facts outside itself:
     descale is amax / 448 in fp32, and its codes equal a brute-force nearest
     value search over the decoder's table with ties to the even code;
   * the oracle's dequantiser returns code value times descale: the amax
-    element comes back as amax, and every element within half an E4M3 step.
+    element comes back as amax, and every element within half an E4M3 step;
+  * the same for the E5M2 gradient format of the fp8 backward pass (section
+    10): the decoder exhaustively against torch.float8_e5m2, the amax
+    quantiser against a brute-force nearest-even search, the round trip.
 """
 
 import math
@@ -197,3 +200,83 @@ def test_dequantise_is_code_value_times_descale():
     np.testing.assert_array_equal(got, vals[ok] * d)
     assert e4m3.dequantise(np.array([0x7E], dtype=np.uint8), d)[0] == 448.0 * d
     assert e4m3.dequantise(np.array([0x01], dtype=np.uint8), 2.0)[0] == 2.0 ** -8
+
+
+# ------------------------------------------------------- e5m2 (fp8 gradients)
+
+def test_e5m2_decoder_exhaustive_against_torch():
+    from oracle import e5m2
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e5m2.decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]
+    np.testing.assert_array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7B] == 57344.0 and ours[0x7C] == np.inf and ours[0xFC] == -np.inf
+    assert ours[0x01] == 2.0 ** -16 and ours[0x04] == 2.0 ** -14 and ours[0x3C] == 1.0
+
+
+def _e5m2_encode_brute_force(y):
+    """Nearest finite E5M2 value (|y| <= 57344), ties to the even mantissa."""
+    from oracle import e5m2
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e5m2.decode(codes)
+    keep = np.isfinite(vals)
+    codes, vals = codes[keep], vals[keep]
+    out = np.empty(np.shape(y), dtype=np.uint8)
+    for idx, x in np.ndenumerate(np.asarray(y, dtype=np.float64)):
+        dist = np.abs(vals - x)
+        cand = codes[dist == dist.min()]
+        if len(cand) > 1:
+            nz = [c for c in cand if e5m2.decode_code(c) != 0.0]
+            if nz:
+                cand = [c for c in cand if (c & 1) == 0] or list(cand)
+            else:
+                cand = [0x80 if math.copysign(1.0, x) < 0 else 0x00]
+        out[idx] = cand[0]
+    return out
+
+
+def test_e5m2_quantiser_matches_brute_force_and_saturates():
+    g = torch.Generator().manual_seed(8)
+    x = torch.randn(3000, generator=g, dtype=torch.float32) * 0.3
+    codes, descale = sdpa_inputs.quantise_e5m2(x)
+    s = np.float32(sdpa_inputs.E5M2_MAX) / np.float32(float(x.abs().max()))
+    y = np.clip(x.numpy() * s, -57344.0, 57344.0)
+    np.testing.assert_array_equal(codes.numpy(), _e5m2_encode_brute_force(y))
+    # amax 57344 gives a scale of exactly 1: ties go to the even mantissa (53248 lies halfway between
+    # 49152 and 57344), and the largest finite value stays
+    t = torch.tensor([1.125, 1.375, 3.5 * 2.0 ** -16, 2.0 ** -17, 53248.0, 57344.0, -1.125, 2.0 ** -18],
+                     dtype=torch.float32)
+    codes, descale = sdpa_inputs.quantise_e5m2(t)
+    assert descale == 1.0
+    from oracle import e5m2
+    np.testing.assert_array_equal(e5m2.decode(codes.numpy()),
+                                  [1.0, 1.5, 2.0 ** -14, 0.0, 49152.0, 57344.0, -1.0, 0.0])
+
+
+def test_e5m2_dequantise_round_trips_within_half_a_step():
+    from oracle import e5m2
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn(5000, generator=g, dtype=torch.float32) * 0.05
+    codes, descale = sdpa_inputs.quantise_e5m2(x)
+    back = e5m2.dequantise(codes.numpy(), descale)
+    xs = x.double().numpy()
+    i = int(np.abs(xs).argmax())
+    assert abs(abs(back[i]) - np.abs(xs).max()) <= 4 * 2.0 ** -24 * np.abs(xs).max()
+    y = np.abs(xs) / descale
+    # half a step: 2^(e - 3) for |x s| in [2^e, 2^(e+1)), e >= -14; 2^-17 below
+    step_half = np.where(y >= 2.0 ** -14, 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** -14))) - 3), 2.0 ** -17)
+    assert np.all(np.abs(back - xs) <= (step_half * (1 + 1e-6) + 1e-7 * y) * descale)
+    assert e5m2.dequantise(np.array([0x3C], dtype=np.uint8), 0.5)[0] == 0.5
+
+
+def test_fp8_gradient_draw_is_the_bf16_gradient_stream():
+    w = sdpa_inputs.custom(1, 2, 1, 40, 40, 64, "fp8", True, seed=77)
+    codes, descale = sdpa_inputs.draw_grad_fp8(w)
+    ref = sdpa_inputs.draw_grad(w).float()  # same N(0,1) stream, rounded to bf16
+    from oracle import e5m2
+    back = torch.from_numpy(e5m2.dequantise(codes.numpy(), descale)).float()
+    assert codes.shape == (1, 2, 40, 64) and codes.dtype == torch.uint8
+    assert float((back - ref).abs().max()) <= 0.13 * float(ref.abs().max())
