@@ -187,48 +187,6 @@ int attn_fwd_splitkv_plan(int B, int Hq, int Hkv, int Sq, int Sk, int d, int num
                           int* splits_used, size_t* workspace_bytes);
 
 /*
- * attn_bwd -- gradients of the attention forward (the backward pass the
- * article "Self-attention, CUDA kernels and FlashAttention", section 3,
- * describes: the attention weights are recomputed tile by tile from the
- * forward's per-row log-sum-exp instead of being stored). For a loss L with
- * dout = dL/dO:
- *
- *   P = exp(scale Q K^T - lse)  (masked pairs 0)    dV = P^T dout
- *   dS = P * (dout V^T - rowsum(dout * O))          dQ = scale dS K
- *   dK = scale dS^T Q
- *
- * summed over the query heads that share a KV head (GQA/MQA). The mask, the
- * head mapping and the layouts are those of attn_fwd.
- *
- *   q, k, v   the forward's inputs; o, lse its outputs (lse is required);
- *   dout      dL/dO, layout of o;
- *   dq        output, layout of q; dk, dv outputs, layout of k / v. Every
- *             element is written (a KV head's gradient is the sum over its
- *             query heads, computed without atomics);
- *   d         64 or 128;
- *   dtype     ATTN_BF16 only: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse;
- *   workspace device memory owned by the caller, 16-byte aligned, at least
- *             attn_bwd_workspace_size bytes: 2*B*Hq*Sq floats (the per-row
- *             rowsum(dout * O), then lse * log2(e)), and, when the query
- *             heads of a KV head are split into s > 1 subsets (groups of 8 or
- *             more heads on grids under 512 dK/dV workgroups, e.g. MQA), from
- *             the next 16-byte boundary the fp32 partial dK and dV of every
- *             subset (2*s*B*Hkv*Sk*d floats), summed in subset order;
- *             contents on entry ignored, unspecified on return; two calls in
- *             flight need two workspaces.
- *   Other arguments as attn_fwd.
- *
- * Returns ATTN_OK or a negative status: ATTN_ERR_NULL if any of q, k, v, o,
- * dout, lse, dq, dk, dv is NULL, ATTN_ERR_WORKSPACE for a missing, misaligned
- * or short workspace, the other codes as attn_fwd.
- */
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-             void* dq, void* dk, void* dv,
-             int B, int Hq, int Hkv, int Sq, int Sk, int d,
-             float scale, int causal, int dtype,
-             void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/*
  * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv without a workspace argument,
  * for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. Same
@@ -256,10 +214,90 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
                              int B, int Hq, int Hkv, int Sq, int Sk, int d,
                              float scale, int causal, int dtype, int num_splits, hipStream_t stream);
 
+/*
+ * attn_bwd -- gradients of the attention forward (the backward pass the
+ * article "Self-attention, CUDA kernels and FlashAttention", section 3,
+ * describes: the attention weights are recomputed tile by tile from the
+ * forward's per-row log-sum-exp instead of being stored). For a loss L with
+ * dout = dL/dO:
+ *
+ *   P = exp(scale Q K^T - lse)  (masked pairs 0)    dV = P^T dout
+ *   dS = P * (dout V^T - rowsum(dout * O))          dQ = scale dS K
+ *   dK = scale dS^T Q
+ *
+ * summed over the query heads that share a KV head (GQA/MQA). The mask, the
+ * head mapping and the layouts are those of attn_fwd.
+ *
+ *   q, k, v   the forward's inputs; o, lse its outputs (lse is required);
+ *   dout      dL/dO, layout of o;
+ *   dq        output, layout of q; dk, dv outputs, layout of k / v. Every
+ *             element is written (a KV head's gradient is the sum over its
+ *             query heads, computed without atomics);
+ *   dtype     ATTN_BF16: bf16 q, k, v, o, dout, dq, dk, dv, d in {64, 128};
+ *             ATTN_F32: fp32 q, k, v, o, dout, dq, dk, dv, d in {32, 64, 128}
+ *             (fp32 matrix cores throughout); lse is fp32 in both;
+ *   workspace device memory owned by the caller, 16-byte aligned, at least
+ *             attn_bwd_workspace_size bytes (that size serves both dtypes):
+ *             2*B*Hq*Sq floats (the per-row rowsum(dout * O), then
+ *             lse * log2(e)), and, for bf16 when the query heads of a KV head
+ *             are split into s > 1 subsets (groups of 8 or more heads on grids
+ *             under 512 dK/dV workgroups, e.g. MQA), from the next 16-byte
+ *             boundary the fp32 partial dK and dV of every subset
+ *             (2*s*B*Hkv*Sk*d floats), summed in subset order; contents on
+ *             entry ignored, unspecified on return; two calls in flight need
+ *             two workspaces.
+ *   Other arguments as attn_fwd.
+ *
+ * Returns ATTN_OK or a negative status: ATTN_ERR_NULL if any of q, k, v, o,
+ * dout, lse, dq, dk, dv is NULL, ATTN_ERR_WORKSPACE for a missing, misaligned
+ * or short workspace, the other codes as attn_fwd.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d,
+             float scale, int causal, int dtype,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* attn_bwd_workspace_size -- host-only: the workspace bytes attn_bwd needs
- * for these sizes (*workspace_bytes, may be NULL). Returns ATTN_OK or the
- * size error attn_bwd would return. */
+ * for these sizes (*workspace_bytes, may be NULL), for either dtype. Returns
+ * ATTN_OK or the size error attn_bwd would return. */
 int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes);
+
+/*
+ * attn_bwd_fp8 -- attn_bwd for fp8 inputs in the codelab's fp8 recipe
+ * (section 10: E4M3 for the forward tensors, E5M2 for the gradients, each
+ * with a per-tensor scale): the same gradients, of the real values
+ *
+ *   Q = descale_q * q8,  K = descale_k * k8,  V = descale_v * v8,
+ *   dO = descale_do * dout8.
+ *
+ *   q8, k8, v8  device uint8 e4m3fn codes, layouts as attn_fwd;
+ *   o           device bfloat16 [B, Hq, Sq, d], the output of attn_fwd_fp8
+ *               for these inputs; lse its fp32 log-sum-exp (required);
+ *   dout8       device uint8 e5m2 codes of dL/dO, layout of o;
+ *   dq, dk, dv  device bfloat16 outputs (real values), layouts of q / k / v;
+ *   descale_*   finite and > 0;
+ *   d           64 or 128;
+ *   workspace   device memory owned by the caller, 16-byte aligned, at least
+ *               attn_bwd_fp8_workspace_size bytes: attn_bwd's workspace, then
+ *               bf16 copies of q8, dout8, k8 and v8 (each code widened, which
+ *               is exact); contents on entry ignored, unspecified on return.
+ *   Other arguments as attn_bwd.
+ *
+ * The codes are widened to bf16 and the products run on bf16 matrix cores
+ * with fp32 accumulation; the descales fold into the softmax scale and the
+ * output factors. Returns as attn_bwd.
+ */
+int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const void* o, const void* dout8,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 float descale_q, float descale_k, float descale_v, float descale_do,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_bwd_fp8_workspace_size -- host-only: the workspace bytes attn_bwd_fp8
+ * needs for these sizes (*workspace_bytes, may be NULL). Returns ATTN_OK or
+ * the size error attn_bwd_fp8 would return. */
+int attn_bwd_fp8_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes);
 
 /* attn_strerror -- static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

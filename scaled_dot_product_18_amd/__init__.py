@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import AttnError, ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3  # noqa: F401
 
-__all__ = ["fwd", "fwd_fp8", "fwd_splitkv", "splitkv_plan", "bwd", "AttnError", "library_path", "version",
+__all__ = ["fwd", "fwd_fp8", "fwd_splitkv", "splitkv_plan", "bwd", "bwd_fp8", "AttnError", "library_path", "version",
            "require_library"]
 
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
@@ -194,42 +194,90 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     return out, lse
 
 
+def _check_bwd_shapes(q, o, dout, lse, B, Hq, Sq):
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor of q's shape on q's device")
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [B, Hq, Sq] tensor the forward returned")
+
+
+def _workspace(workspace, nbytes, device):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace
+
+
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
         workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Gradients (dq, dk, dv) of the attention forward for bfloat16 tensors.
+    """Gradients (dq, dk, dv) of the attention forward for bfloat16 or float32 tensors.
 
     ``o`` and ``lse`` are what :func:`fwd` returned for (q, k, v) with
     ``want_lse=True`` and the same ``causal`` and ``scale``; ``dout`` is the
     gradient of the loss with respect to ``o``. dk and dv have k's shape (with
     GQA/MQA they sum over the query heads that share a KV head). ``workspace``
-    (2*B*Hq*Sq float32) is allocated here when not given.
+    is allocated here when not given.
     """
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"bwd takes bfloat16 tensors, {name} is {t.dtype}")
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"bwd takes bfloat16 or float32 tensors, q is {dt}")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != dt:
+            raise ValueError(f"bwd takes tensors of one dtype: q is {dt}, {name} is {t.dtype}")
     B, Hq, Hkv, Sq, Sk, d = _shapes(q, k, v)
     _dense_only(q, k, v)
-    for name, t in (("o", o), ("dout", dout)):
-        if t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous tensor of q's shape on q's device")
-    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be the contiguous float32 [B, Hq, Sq] tensor fwd returned")
+    _check_bwd_shapes(q, o, dout, lse, B, Hq, Sq)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st, nbytes = _lib.attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d)
     _lib.check(st)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
-    elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    workspace = _workspace(workspace, nbytes, q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _lib.check(_lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                             B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_BF16,
+                             B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_BF16 if dt == torch.bfloat16 else ATTN_F32,
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream))
+    return dq, dk, dv
+
+
+def bwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+            dout8: torch.Tensor, descale_q: float, descale_k: float, descale_v: float, descale_do: float, *,
+            causal: bool = False, scale: Optional[float] = None,
+            workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv; bfloat16, real values) for fp8 inputs: e4m3fn codes
+    q8/k8/v8 and e5m2 codes dout8 (uint8 tensors) with per-tensor descales, the
+    bfloat16 ``o`` and float32 ``lse`` that :func:`fwd_fp8` returned."""
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8), ("dout8", dout8)):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"bwd_fp8 takes uint8 fp8 codes, {name} is {t.dtype}")
+    if o.dtype != torch.bfloat16:
+        raise ValueError(f"bwd_fp8 takes the bfloat16 forward output, o is {o.dtype}")
+    B, Hq, Hkv, Sq, Sk, d = _shapes(q8, k8, v8)
+    _dense_only(q8, k8, v8)
+    if dout8.shape != q8.shape or not dout8.is_contiguous() or dout8.device != q8.device:
+        raise ValueError("dout8 must be a contiguous tensor of q8's shape on q8's device")
+    if o.shape != q8.shape or not o.is_contiguous() or o.device != q8.device:
+        raise ValueError("o must be a contiguous tensor of q8's shape on q8's device")
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q8.device:
+        raise ValueError("lse must be the contiguous float32 [B, Hq, Sq] tensor fwd_fp8 returned")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st, nbytes = _lib.attn_bwd_fp8_workspace_size(B, Hq, Hkv, Sq, Sk, d)
+    _lib.check(st)
+    workspace = _workspace(workspace, nbytes, q8.device)
+    dq = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    dk = torch.empty(k8.shape, dtype=torch.bfloat16, device=q8.device)
+    dv = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device)
+    stream = torch.cuda.current_stream(q8.device).cuda_stream
+    _lib.check(_lib.attn_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), dout8.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 B, Hq, Hkv, Sq, Sk, d, scale, causal, float(descale_q), float(descale_k),
+                                 float(descale_v), float(descale_do),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream))
     return dq, dk, dv
 
 

@@ -74,6 +74,11 @@ def load() -> ctypes.CDLL:
         lib.attn_bwd.restype = i
         lib.attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
         lib.attn_bwd_workspace_size.restype = i
+        lib.attn_bwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, f, f, f, f, vp, sz,
+                                     vp]
+        lib.attn_bwd_fp8.restype = i
+        lib.attn_bwd_fp8_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
+        lib.attn_bwd_fp8_workspace_size.restype = i
         lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int64), f, i,
                                          i, f, f, f, vp]
         lib.attn_fwd_strided.restype = i
@@ -137,6 +142,20 @@ def attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d):
     """(status, workspace_bytes) of the host-only size query."""
     nbytes = ctypes.c_size_t(0)
     st = load().attn_bwd_workspace_size(B, Hq, Hkv, Sq, Sk, d, ctypes.byref(nbytes))
+    return st, nbytes.value
+
+
+def attn_bwd_fp8(q8, k8, v8, o, dout8, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, causal, ds_q, ds_k, ds_v,
+                 ds_do, ws, ws_bytes, stream) -> int:
+    """Raw call with integer pointers; returns the status code."""
+    return load().attn_bwd_fp8(q8, k8, v8, o, dout8, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, int(causal), ds_q,
+                               ds_k, ds_v, ds_do, ws, ws_bytes, stream)
+
+
+def attn_bwd_fp8_workspace_size(B, Hq, Hkv, Sq, Sk, d):
+    """(status, workspace_bytes) of the host-only size query."""
+    nbytes = ctypes.c_size_t(0)
+    st = load().attn_bwd_fp8_workspace_size(B, Hq, Hkv, Sq, Sk, d, ctypes.byref(nbytes))
     return st, nbytes.value
 
 

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_pp.hip", "attn_fwd_fp8_pp.hip", "attn_fwd_mfma.hip",
-           "attn_fwd_f32.hip", "attn_fwd_splitkv.hip", "attn_bwd.hip"]
+           "attn_fwd_f32.hip", "attn_fwd_splitkv.hip", "attn_bwd.hip", "attn_bwd_f32.hip"]
 
 
 def _hipcc() -> str:

@@ -197,6 +197,87 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   return launch_status(sdpa18::launch_attn_fp8(p, d, causal != 0, stream));
 }
 
+// Workspace of attn_bwd_fp8: the bf16 backward's, then bf16 copies of q, k,
+// v and dout (the fp8 codes widened), each from a 16-byte boundary.
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+size_t bwd_fp8_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
+  const size_t nq = (size_t)B * Hq * Sq * d, nk = (size_t)B * Hkv * Sk * d;
+  return align16(bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d)) + 2 * align16(2 * nq) + 2 * align16(2 * nk);
+}
+
+// Shared path of attn_bwd (bf16, fp32) and attn_bwd_fp8 (dtype ATTN_FP8_E4M3:
+// e4m3 q, k, v and e5m2 dout with per-tensor descales, bf16 o and outputs).
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+               int dtype, float ds_q, float ds_k, float ds_v, float ds_do, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  if (o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return ATTN_ERR_NULL;
+  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F32 && d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if ((int64_t)((Sk + 63) / 64) * B * Hkv >= INT32_MAX) return ATTN_ERR_SHAPE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
+  if (!positive_finite(scale) || !positive_finite(ds_q) || !positive_finite(ds_k) || !positive_finite(ds_v) ||
+      !positive_finite(ds_do))
+    return ATTN_ERR_SCALE;
+  const float qk = scale * ds_q * ds_k;
+  if (!positive_finite(qk * kLog2e) || !positive_finite(scale * ds_do * ds_v * ds_k) ||
+      !positive_finite(scale * ds_do * ds_v * ds_q))
+    return ATTN_ERR_SCALE;
+  const size_t rows = (size_t)B * Hq * Sq;
+  const size_t need = dtype == ATTN_FP8_E4M3 ? bwd_fp8_workspace_bytes(B, Hq, Hkv, Sq, Sk, d)
+                      : dtype == ATTN_F32    ? 2 * rows * sizeof(float)
+                                             : bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  sdpa18::BwdParams bp;
+  bp.q = q;
+  bp.k = k;
+  bp.v = v;
+  bp.o = o;
+  bp.dout = dout;
+  bp.lse = lse;
+  bp.delta = static_cast<float*>(workspace);
+  bp.lse2 = static_cast<float*>(workspace) + rows;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.B = B;
+  bp.Hq = Hq;
+  bp.Hkv = Hkv;
+  bp.Sq = Sq;
+  bp.Sk = Sk;
+  bp.group = Hq / Hkv;
+  bp.causal_off = causal ? Sk - Sq : 0;
+  bp.qk_scale_log2 = qk * kLog2e;
+  // Real values: q = ds_q q', k = ds_k k', v = ds_v v', dout = ds_do dout'. With
+  // delta' = rowsum(dout' o) / ds_v and dS' = P (dout' v'^T - delta'), the
+  // gradients are dS = ds_do ds_v dS', dQ = scale dS K, dK = scale dS^T Q, dV = P^T dout.
+  bp.delta_mul = 1.0f / ds_v;
+  bp.dq_mul = scale * ds_do * ds_v * ds_k;
+  bp.dk_mul = scale * ds_do * ds_v * ds_q;
+  bp.dv_mul = ds_do;
+  bp.n_qtiles = (Sq + 127) / 128;
+  bp.n_ktiles = (Sk + 127) / 128;
+  if (dtype == ATTN_F32) {
+    bp.kv_split = 1;
+    bp.dkv_part = nullptr;
+    return launch_status(sdpa18::launch_attn_bwd_f32(bp, d, causal != 0, stream));
+  }
+  bp.kv_split = sdpa18::bwd_kv_split(B, Hkv, Sk, Hq / Hkv);
+  bp.dkv_part = bp.kv_split > 1
+                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bwd_part_offset(B, Hq, Sq))
+                    : nullptr;
+  if (dtype == ATTN_BF16) return launch_status(sdpa18::launch_attn_bwd_bf16(bp, d, causal != 0, stream));
+  const size_t nq = (size_t)B * Hq * Sq * d, nk = (size_t)B * Hkv * Sk * d;
+  unsigned char* w = static_cast<unsigned char*>(workspace) + align16(bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d));
+  unsigned char* q16 = w;
+  unsigned char* do16 = q16 + align16(2 * nq);
+  unsigned char* k16 = do16 + align16(2 * nq);
+  unsigned char* v16 = k16 + align16(2 * nk);
+  return launch_status(sdpa18::launch_attn_bwd_fp8(bp, q16, k16, v16, do16, d, causal != 0, stream));
+}
+
 // Scratch of attn_fwd_splitkv_noalloc: the key chunks' partial outputs and
 // log-sum-exps, in a static device array instead of caller memory. Every GPU
 // the library runs on holds its own copy until the process ends; in host code
@@ -314,54 +395,33 @@ int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* 
 int attn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
   if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (d != 32 && d != 64 && d != 128) return ATTN_ERR_HEADDIM;
   if (workspace_bytes != nullptr) *workspace_bytes = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
+  return ATTN_OK;
+}
+
+int attn_bwd_fp8_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk, int d, size_t* workspace_bytes) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (workspace_bytes != nullptr) *workspace_bytes = bwd_fp8_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
   return ATTN_OK;
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
-  if (o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
-    return ATTN_ERR_NULL;
-  int st = validate(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal);
-  if (st != ATTN_OK) return st;
-  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
-  if ((int64_t)((Sk + 127) / 128) * B * Hkv >= INT32_MAX) return ATTN_ERR_SHAPE;
-  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
-  if (!positive_finite(scale) || !positive_finite(scale * kLog2e)) return ATTN_ERR_SCALE;
-  const size_t rows = (size_t)B * Hq * Sq;
-  const size_t need = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  sdpa18::BwdParams bp;
-  bp.q = q;
-  bp.k = k;
-  bp.v = v;
-  bp.o = o;
-  bp.dout = dout;
-  bp.lse = lse;
-  bp.delta = static_cast<float*>(workspace);
-  bp.lse2 = static_cast<float*>(workspace) + rows;
-  bp.dq = dq;
-  bp.dk = dk;
-  bp.dv = dv;
-  bp.B = B;
-  bp.Hq = Hq;
-  bp.Hkv = Hkv;
-  bp.Sq = Sq;
-  bp.Sk = Sk;
-  bp.group = Hq / Hkv;
-  bp.causal_off = causal ? Sk - Sq : 0;
-  bp.scale = scale;
-  bp.qk_scale_log2 = scale * kLog2e;
-  bp.n_qtiles = (Sq + 127) / 128;
-  bp.n_ktiles = (Sk + 127) / 128;
-  bp.kv_split = sdpa18::bwd_kv_split(B, Hkv, Sk, Hq / Hkv);
-  bp.dkv_part = bp.kv_split > 1
-                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bwd_part_offset(B, Hq, Sq))
-                    : nullptr;
-  return launch_status(sdpa18::launch_attn_bwd_bf16(bp, d, causal != 0, stream));
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  return bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, causal, dtype, 1.0f, 1.0f, 1.0f,
+                    1.0f, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const void* o, const void* dout8, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 float descale_q, float descale_k, float descale_v, float descale_do, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(q8, k8, v8, o, dout8, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, scale, causal, ATTN_FP8_E4M3,
+                    descale_q, descale_k, descale_v, descale_do, workspace, workspace_bytes, stream);
 }
 
 const char* attn_strerror(int status) {

@@ -158,7 +158,7 @@ void attn_bwd_delta_kernel(const BwdParams p) {
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < rows && part == 0) {
-    p.delta[row] = acc;
+    p.delta[row] = acc * p.delta_mul;
     p.lse2[row] = p.lse[row] * kLog2e;
   }
 }
@@ -311,11 +311,11 @@ void attn_bwd_dq_kernel(const BwdParams p) {
     __syncthreads();
   }
 
-  // dQ = scale * acc. The K/V tiles are idle after the last barrier: wave w
+  // dQ = dq_mul * acc. The K/V tiles are idle after the last barrier: wave w
   // stages its 32 rows in 32 * RB bytes of them.
   if (!wave_active) return;
   unsigned char* stage = (wave < 2 ? k_lds0 : v_lds0) + (wave & 1) * (32 * C::RB);
-  store_tile<D>(acc, p.scale, stage, (unsigned char*)p.dq + (qo_row0 + qw) * C::RB, p.Sq - qw, lane);
+  store_tile<D>(acc, p.dq_mul, stage, (unsigned char*)p.dq + (qo_row0 + qw) * C::RB, p.Sq - qw, lane);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -518,19 +518,20 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * db + 8 * q4 + 4 * g;
-        *(float4*)(pk + d) = float4{dk[db][4 * q4] * p.scale, dk[db][4 * q4 + 1] * p.scale,
-                                    dk[db][4 * q4 + 2] * p.scale, dk[db][4 * q4 + 3] * p.scale};
-        *(float4*)(pv + d) = float4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+        *(float4*)(pk + d) = float4{dk[db][4 * q4] * p.dk_mul, dk[db][4 * q4 + 1] * p.dk_mul,
+                                    dk[db][4 * q4 + 2] * p.dk_mul, dk[db][4 * q4 + 3] * p.dk_mul};
+        *(float4*)(pv + d) = float4{dv[db][4 * q4] * p.dv_mul, dv[db][4 * q4 + 1] * p.dv_mul,
+                                    dv[db][4 * q4 + 2] * p.dv_mul, dv[db][4 * q4 + 3] * p.dv_mul};
       }
     return;
   }
-  // dK = scale * dk, dV = dv. The Q and dO tiles are idle after the last
-  // barrier: wave w stages its 32 dK rows in the Q tiles and its dV rows in the
-  // dO tiles.
+  // dK = dk_mul * dk, dV = dv_mul * dv. The Q and dO tiles are idle after the
+  // last barrier: wave w stages its 32 dK rows in the Q tiles and its dV rows
+  // in the dO tiles.
   const int half = (wave & 1) * (32 * C::RB);
-  store_tile<D>(dk, p.scale, (wave < 2 ? q_lds0 : q_lds1) + half, (unsigned char*)p.dk + (kv_row0 + kw) * C::RB,
+  store_tile<D>(dk, p.dk_mul, (wave < 2 ? q_lds0 : q_lds1) + half, (unsigned char*)p.dk + (kv_row0 + kw) * C::RB,
                 p.Sk - kw, lane);
-  store_tile<D>(dv, 1.0f, (wave < 2 ? o_lds0 : o_lds1) + half, (unsigned char*)p.dv + (kv_row0 + kw) * C::RB,
+  store_tile<D>(dv, p.dv_mul, (wave < 2 ? o_lds0 : o_lds1) + half, (unsigned char*)p.dv + (kv_row0 + kw) * C::RB,
                 p.Sk - kw, lane);
 }
 
@@ -580,7 +581,68 @@ hipError_t launch_d(const BwdParams& bp, hipStream_t stream) {
                          rargs, 0, stream);
 }
 
+// fp8 codes -> bf16, 16 per thread: E4M3 (the forward format) for q, k, v and
+// E5M2 (the gradient format) for dout. Both are exact: bf16 has more exponent
+// range and more mantissa bits than either.
+template <bool E5M2>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void attn_bwd_widen_kernel(const unsigned char* src, unsigned char* dst, size_t n16) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 x = *(const u32x4*)(src + 16 * i);
+  u32x4 lo, hi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    typedef bf16_t bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 a, b;
+    if (E5M2) {
+      a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x[w], 1.0f, false);
+      b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x[w], 1.0f, true);
+    } else {
+      a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false);
+      b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true);
+    }
+    const uint32_t wa = __builtin_bit_cast(uint32_t, a), wb = __builtin_bit_cast(uint32_t, b);
+    if (w < 2) {
+      lo[2 * w] = wa;
+      lo[2 * w + 1] = wb;
+    } else {
+      hi[2 * (w - 2)] = wa;
+      hi[2 * (w - 2) + 1] = wb;
+    }
+  }
+  *(u32x4*)(dst + 32 * i) = lo;
+  *(u32x4*)(dst + 32 * i + 16) = hi;
+}
+
+template <bool E5M2>
+hipError_t widen(const void* src, void* dst, size_t n, hipStream_t stream) {
+  // n is a multiple of 16 (rows of 32, 64 or 128 elements)
+  const size_t n16 = n / 16;
+  const unsigned char* s8 = (const unsigned char*)src;
+  unsigned char* d8 = (unsigned char*)dst;
+  void* args[] = {&s8, &d8, (void*)&n16};
+  return hipLaunchKernel((const void*)&attn_bwd_widen_kernel<E5M2>, dim3((unsigned)((n16 + 255) / 256)), dim3(256),
+                         args, 0, stream);
+}
+
 }  // namespace bwd
+
+hipError_t launch_attn_bwd_fp8(const BwdParams& bp, void* q16, void* k16, void* v16, void* do16, int d, bool causal,
+                               hipStream_t stream) {
+  const size_t nq = (size_t)bp.B * bp.Hq * bp.Sq * d, nk = (size_t)bp.B * bp.Hkv * bp.Sk * d;
+  hipError_t e = bwd::widen<false>(bp.q, q16, nq, stream);
+  if (e == hipSuccess) e = bwd::widen<false>(bp.k, k16, nk, stream);
+  if (e == hipSuccess) e = bwd::widen<false>(bp.v, v16, nk, stream);
+  if (e == hipSuccess) e = bwd::widen<true>(bp.dout, do16, nq, stream);
+  if (e != hipSuccess) return e;
+  BwdParams w = bp;
+  w.q = q16;
+  w.k = k16;
+  w.v = v16;
+  w.dout = do16;
+  return launch_attn_bwd_bf16(w, d, causal, stream);
+}
 
 hipError_t launch_attn_bwd_bf16(const BwdParams& bp, int d, bool causal, hipStream_t stream) {
   if (d == 128) return causal ? bwd::launch_d<128, true>(bp, stream) : bwd::launch_d<128, false>(bp, stream);

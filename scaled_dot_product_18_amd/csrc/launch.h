@@ -65,8 +65,13 @@ struct BwdParams {
   int B, Hq, Hkv, Sq, Sk;
   int group;            // Hq / Hkv
   int causal_off;       // Sk - Sq under the causal mask, else 0
-  float scale;          // multiplier of the dot products
-  float qk_scale_log2;  // scale * log2(e)
+  float qk_scale_log2;  // multiplier of the dot products of the q, k arrays, times log2(e)
+  // Factors that turn the arrays' values into the real ones (all 1 but the
+  // dot-product scale unless q, k, v, dout are fp8 codes with descales):
+  float delta_mul;      // delta = delta_mul * rowsum(dout * o), in the units of dout . v^T
+  float dq_mul;         // dQ = dq_mul * sum dS K   (scale, times descales for fp8)
+  float dk_mul;         // dK = dk_mul * sum dS^T Q
+  float dv_mul;         // dV = dv_mul * sum P^T dout
   int n_qtiles;         // ceil(Sq / 128): dQ workgroups per (batch, query head)
   int n_ktiles;         // ceil(Sk / 128): dK/dV workgroups per (batch, KV head) and query-head subset
   int kv_split;         // query-head subsets per KV head in the dK/dV kernel (1: no partial sums)
@@ -85,5 +90,16 @@ inline int bwd_kv_split(int B, int Hkv, int Sk, int group) {
 
 // bf16, d in {64, 128}: delta, then dQ, then dK and dV, on one stream.
 hipError_t launch_attn_bwd_bf16(const BwdParams& bp, int d, bool causal, hipStream_t stream);
+
+// fp8 inputs: q, k, v are e4m3fn codes and dout e5m2 codes (bp.q, bp.k,
+// bp.v, bp.dout point at them), o is bf16. The codes are first widened to
+// bf16 (exactly) into q16, k16, v16, do16 (each as many bf16 elements as the
+// corresponding input), then the bf16 kernels run on the widened copies.
+hipError_t launch_attn_bwd_fp8(const BwdParams& bp, void* q16, void* k16, void* v16, void* do16, int d, bool causal,
+                               hipStream_t stream);
+
+// fp32 inputs and outputs, d in {32, 64, 128}: delta, dQ, dK and dV on fp32
+// matrix cores.
+hipError_t launch_attn_bwd_f32(const BwdParams& bp, int d, bool causal, hipStream_t stream);
 
 }  // namespace sdpa18

@@ -32,7 +32,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _header_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp8",
+    assert _header_functions() == ["attn_bwd", "attn_bwd_fp8", "attn_bwd_fp8_workspace_size",
+                                   "attn_bwd_workspace_size", "attn_fwd", "attn_fwd_fp8",
                                    "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_plan",
                                    "attn_fwd_strided", "attn_strerror", "attn_version"]
 
@@ -193,12 +194,12 @@ def test_bwd_validation_errors(lib):
                  a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"],
                  None)
 
-    assert call(dtype=0) == -6 and call(dtype=2) == -6
+    assert call(dtype=2) == -6 and call(dtype=3) == -6
     for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
         assert call(**{name: None}) == -1, name
     assert call(Sk=0) == -2
     assert call(Hkv=3) == -3
-    assert call(d=32) == -4
+    assert call(d=32) == -4 and call(d=48) == -4 and call(dtype=0, d=48) == -4  # bf16: 64, 128; fp32: 32, 64, 128
     assert call(Sq=9) == -5
     assert call(scale=float("nan")) == -7
     assert call(dk=P + 2) == -8 and call(do=P + 8) == -8
@@ -214,6 +215,35 @@ def test_bwd_validation_errors(lib):
     assert st == 0 and nbytes == 2 * 4 * 8 * 4
     assert lib.attn_bwd_workspace_size(1, 3, 2, 8, 8, 128)[0] == -3
     assert lib.attn_bwd_workspace_size(1, 4, 2, 8, 8, 96)[0] == -4
+
+
+def test_bwd_fp8_validation_errors(lib):
+    f = lib.load().attn_bwd_fp8
+    ok = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.1,
+              causal=1, dsq=0.01, dsk=0.02, dsv=0.03, dsdo=1e-4, ws=P, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                 a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["dsq"], a["dsk"], a["dsv"],
+                 a["dsdo"], a["ws"], a["ws_bytes"], None)
+
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call(**{name: None}) == -1, name
+    assert call(B=0) == -2
+    assert call(Hkv=3) == -3
+    assert call(d=32) == -4
+    assert call(Sq=9) == -5
+    for name in ("dsq", "dsk", "dsv", "dsdo"):
+        assert call(**{name: 0.0}) == -7 and call(**{name: float("inf")}) == -7, name
+    assert call(scale=-1.0) == -7
+    assert call(dq=P + 2) == -8
+    # workspace: the bf16 backward's, then bf16 copies of q8, dout8 (4*8*128 codes each)
+    # and k8, v8 (2*8*128 codes each), every region from a 16-byte boundary
+    st, nbytes = lib.attn_bwd_fp8_workspace_size(1, 4, 2, 8, 8, 128)
+    assert st == 0 and nbytes == 2 * 4 * 8 * 4 + 2 * (2 * 4 * 8 * 128) + 2 * (2 * 2 * 8 * 128)
+    assert call(ws=None) == -10 and call(ws=P + 8) == -10 and call(ws_bytes=nbytes - 1) == -10
+    assert lib.attn_bwd_fp8_workspace_size(1, 4, 2, 8, 8, 32)[0] == -4
 
 
 def test_strided_validation_errors(lib):

@@ -1,0 +1,183 @@
+"""GPU parity of the fp32 and fp8 backward passes against the fp64 gradient oracle.
+
+fp32 (attn_bwd with float32 tensors): the HIP fp32 forward produces O and lse,
+the fp32 backward takes them with a seeded upstream gradient, and dQ, dK, dV
+are compared element by element with oracle.attention_backward on the same
+fp32 values. Every product runs on fp32 matrix cores with fp32 accumulation,
+so the error is that of fp32 sums over at most a few thousand terms (relative
+~1e-6) plus the forward's own O error inside the row statistic delta; the test
+allows max|GPU - oracle| <= 1e-4 * max(1, max|oracle|) per tensor.
+
+fp8 (attn_bwd_fp8): q, k, v are per-tensor amax e4m3fn codes and dO per-tensor
+amax e5m2 codes (the codelab's fp8 recipe, section 10); the oracle runs on the
+dequantised values. The codes are widened exactly and the products run as in
+the bf16 backward, so the bf16 bound applies (P and dS rounded to bf16, bf16
+outputs): 2e-2 * max(1, max|oracle|) per tensor. The backward also takes the
+forward's output O as stored, in bf16, and the real values of fp8 codes times
+an fp32 descale are generally not bf16 numbers, so O carries a rounding of up
+to 2^-9 of each element that the oracle's O does not. It enters
+delta_i = sum_c dO_ic O_ic, hence dS_ij = P_ij (dP_ij - delta_i), by
+|d delta_i| <= 2^-9 sum_c |dO_ic O_ic|, and dQ_i = scale sum_j dS_ij K_j (dK
+likewise with Q) by at most scale * max_i |d delta_i| * max|K| (max|Q|); the
+test adds that term, computed from the inputs with a factor 2 of margin, to
+the dQ and dK bounds. (With a single key, where exact arithmetic gives
+dQ = dK = 0, this term is all of the error.) With unit descales the fp8
+backward must equal the bf16 backward on the decoded codes bit for bit (the
+widening is exact).
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3, e5m2
+from oracle.backward import attention_backward
+import sdpa_inputs
+from parity_util import log
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_FP8 = 2e-2
+
+
+def _compare(name_w, got_all, ref_all, tol, extra=(0.0, 0.0, 0.0)):
+    stats = {}
+    for name, got, r, ex in zip(("dq", "dk", "dv"), got_all, ref_all, extra):
+        x = got.to(torch.float64).cpu().numpy()
+        assert np.isfinite(x).all(), f"{name_w}: non-finite {name}"
+        err = float(np.abs(x - r).max())
+        scale = max(1.0, float(np.abs(r).max()))
+        stats[name] = (float(f"{err:.3g}"), round(scale, 3), float(f"{ex:.3g}"))
+        assert err <= tol * scale + ex, f"{name_w}: {name} max err {err} (scale {scale}, O term {ex}) {stats}"
+    return stats
+
+
+def _run_f32(w):
+    import scaled_dot_product_18_amd as sdpa
+    log(f"[bwd-f32] {w.name}")
+    inp = sdpa_inputs.make_inputs(w)
+    g = sdpa_inputs.draw_grad(w).float()
+    q, k, v, do = (t.cuda() for t in (inp["q"], inp["k"], inp["v"], g))
+    o, lse = sdpa.fwd(q, k, v, causal=w.causal, scale=w.scale, want_lse=True)
+    dq, dk, dv = sdpa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.float32 and dk.dtype == torch.float32
+    ref = attention_backward(*(t.to(torch.float64).numpy() for t in (inp["q"], inp["k"], inp["v"], g)),
+                             w.scale, w.causal)
+    return _compare(w.name, (dq, dk, dv), ref, TOL_F32), (dq, dk, dv), (q, k, v, o, lse, do)
+
+
+S_LIST = [1, 17, 64, 65, 128, 129, 200, 257]
+HEADS = [(4, 4), (4, 2), (4, 1)]
+
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product(S_LIST, (32, 64, 128), (False, True), HEADS)))
+def test_bwd_f32_tails(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    stats, *_ = _run_f32(sdpa_inputs.custom(1, Hq, Hkv, S, S, d, "f32", causal, seed=21000 + S))
+    log(f"  {stats}")
+
+
+@pytest.mark.parametrize("Sq,Sk,d", [(1, 300, 128), (5, 64, 64), (77, 200, 32), (130, 257, 64), (256, 1000, 128)])
+def test_bwd_f32_queries_are_the_last_positions(gpu, Sq, Sk, d):
+    for causal in (True, False):
+        _run_f32(sdpa_inputs.custom(2, 4, 2, Sq, Sk, d, "f32", causal, seed=22000 + Sq + Sk))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_f32_batches_and_groups(gpu, d):
+    stats, *_ = _run_f32(sdpa_inputs.custom(3, 12, 3, 300, 300, d, "f32", True, seed=23000 + d))
+    log(f"  {stats}")
+
+
+def test_bwd_f32_is_deterministic(gpu):
+    import scaled_dot_product_18_amd as sdpa
+    _, first, (q, k, v, o, lse, do) = _run_f32(sdpa_inputs.custom(2, 8, 2, 333, 333, 128, "f32", True, seed=24000))
+    second = sdpa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------ fp8
+
+def _run_fp8(w):
+    import scaled_dot_product_18_amd as sdpa
+    log(f"[bwd-fp8] {w.name}")
+    inp = sdpa_inputs.make_inputs(w)
+    g8, ds_do = sdpa_inputs.draw_grad_fp8(w)
+    q8, k8, v8, do8 = (t.cuda() for t in (inp["q"], inp["k"], inp["v"], g8))
+    ds = (inp["descale_q"], inp["descale_k"], inp["descale_v"])
+    o, lse = sdpa.fwd_fp8(q8, k8, v8, *ds, causal=w.causal, scale=w.scale, want_lse=True)
+    dq, dk, dv = sdpa.bwd_fp8(q8, k8, v8, o, lse, do8, *ds, ds_do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert dq.dtype == torch.bfloat16
+    real = [e4m3.dequantise(inp[n].numpy(), inp["descale_" + n]) for n in ("q", "k", "v")]
+    do_real = e5m2.dequantise(g8.numpy(), ds_do)
+    ref = attention_backward(*real, do_real, w.scale, w.causal)
+    # the bf16 rounding of the stored O inside delta (see the module docstring)
+    ddelta = 2.0 ** -9 * float(np.abs(do_real * o.double().cpu().numpy()).sum(-1).max())
+    extra = (2 * w.scale * ddelta * float(np.abs(real[1]).max()), 2 * w.scale * ddelta * float(np.abs(real[0]).max()),
+             0.0)
+    return _compare(w.name, (dq, dk, dv), ref, TOL_FP8, extra)
+
+
+@pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 65, 129, 257], (64, 128), (False, True),
+                                                                    HEADS + [(8, 1)])))
+def test_bwd_fp8_tails(gpu, S, d, causal, heads):
+    Hq, Hkv = heads
+    stats = _run_fp8(sdpa_inputs.custom(2, Hq, Hkv, S, S, d, "fp8", causal, seed=25000 + S))
+    log(f"  {stats}")
+
+
+@pytest.mark.parametrize("Sq,Sk,d", [(1, 300, 128), (77, 200, 64), (256, 1000, 128)])
+def test_bwd_fp8_queries_are_the_last_positions(gpu, Sq, Sk, d):
+    for causal in (True, False):
+        _run_fp8(sdpa_inputs.custom(2, 4, 2, Sq, Sk, d, "fp8", causal, seed=26000 + Sq + Sk))
+
+
+def test_bwd_fp8_long_causal_gqa(gpu):
+    """A longer causal GQA shape: B2 Hq16 Hkv4 S1024 d128, every element against the oracle."""
+    stats = _run_fp8(sdpa_inputs.custom(2, 16, 4, 1024, 1024, 128, "fp8", True, seed=9000))
+    log(f"  {stats}")
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False), (128, True)])
+def test_bwd_fp8_unit_descales_equal_bf16_on_decoded_codes(gpu, d, causal):
+    """Random codes with descales of 1: the fp8 backward equals the bf16 backward run on the
+    decoded values (e4m3 and e5m2 codes are exact in bf16) bit for bit."""
+    import scaled_dot_product_18_amd as sdpa
+    gen = torch.Generator().manual_seed(27000 + d)
+    B, Hq, Hkv, S = 2, 8, 2, 300
+
+    def codes(shape, fmt):
+        x = torch.randn(shape, generator=gen) * (4.0 if fmt == "e4m3" else 2.0)
+        return x.to(torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2).view(torch.uint8)
+
+    q8, k8, v8 = codes((B, Hq, S, d), "e4m3"), codes((B, Hkv, S, d), "e4m3"), codes((B, Hkv, S, d), "e4m3")
+    do8 = codes((B, Hq, S, d), "e5m2")
+    dev = [t.cuda() for t in (q8, k8, v8, do8)]
+    scale = 0.05
+    o, lse = sdpa.fwd_fp8(dev[0], dev[1], dev[2], 1.0, 1.0, 1.0, causal=causal, scale=scale, want_lse=True)
+    a = sdpa.bwd_fp8(dev[0], dev[1], dev[2], o, lse, dev[3], 1.0, 1.0, 1.0, 1.0, causal=causal, scale=scale)
+    bf = [torch.from_numpy(e4m3.decode(t.numpy())).to(torch.bfloat16).cuda() for t in (q8, k8, v8)]
+    dob = torch.from_numpy(e5m2.decode(do8.numpy())).to(torch.bfloat16).cuda()
+    b = sdpa.bwd(bf[0], bf[1], bf[2], o, lse, dob, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_fp8_errors_raise_through_python(gpu):
+    import scaled_dot_product_18_amd as sdpa
+    z8 = torch.zeros(1, 2, 8, 64, dtype=torch.uint8, device="cuda")
+    o = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 2, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        sdpa.bwd_fp8(z8, z8, z8, o.float(), lse, z8, 1.0, 1.0, 1.0, 1.0)
+    with pytest.raises(sdpa.AttnError) as e:
+        sdpa.bwd_fp8(z8, z8, z8, o, lse, z8, 1.0, 0.0, 1.0, 1.0)
+    assert e.value.status == -7

@@ -97,8 +97,10 @@ def test_bwd_errors_raise_through_python(gpu):
     import scaled_dot_product_18_amd as sdpa
     z = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(1, 2, 8, dtype=torch.float32, device="cuda")
-    with pytest.raises(ValueError):
-        sdpa.bwd(z.float(), z.float(), z.float(), z.float(), lse, z.float())
+    with pytest.raises(ValueError):  # mixed dtypes
+        sdpa.bwd(z.float(), z, z, z, lse, z)
+    with pytest.raises(ValueError):  # fp16 is not a backward dtype
+        sdpa.bwd(z.half(), z.half(), z.half(), z.half(), lse, z.half())
     with pytest.raises(ValueError):
         sdpa.bwd(z, z, z, z, lse[:, :, :4].contiguous(), z)
     with pytest.raises(sdpa.AttnError) as e:
