@@ -12,7 +12,8 @@
 //
 // Work of one wave (32 query rows) over its T key tiles of 64 keys is a chain
 // of phases  M0 V0 M1 V1 ... M(T-1) V(T-1) MT:
-//   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T - m_ref   (32 MFMAs)
+//   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T - m_ref   (32 MFMAs;
+//         M0 has only the scores, 16 MFMAs)
 //   V(m): mask, P(m) = exp2(c S(m)), row sums, reference check
 // A workgroup holds 8 waves, two per SIMD: group A (waves 0-3) runs M phases
 // on even global phases and V phases on odd ones, group B (waves 4-7) the
@@ -20,6 +21,13 @@
 // other keeps the vector unit busy. A workgroup barrier separates global
 // phases. The two waves of a SIMD own adjacent 32-row blocks, so they have the
 // same number of key tiles.
+//
+// Rows of a workgroup: 256 rows of one query head, or, under the causal mask
+// when 2 or 4 query heads share a KV head, 128 or 64 rows of each of them. With
+// one head the causal diagonal gives the four SIMDs 1, 2, 3 and 4 tiles of the
+// last four, and the phase barriers make all of them wait for the fourth; with
+// 64 rows of four heads every wave reads the same K/V tiles and needs the same
+// number of them.
 //
 // K/V tiles: K(n+1) and V(n) are loaded HBM -> LDS (buffer_load ... lds, 2 KB
 // per wave) during global phase 2n and waited for before the barrier
@@ -110,7 +118,7 @@ __device__ __forceinline__ void barrier_after() {
   asm volatile("" ::: "memory");
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, int HP>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE];
@@ -118,37 +126,44 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[TILE];
 
+  // HP query heads of one KV head share the workgroup, BM / HP rows each: SIMD
+  // si serves head si / (4 / HP), and its two waves own adjacent 32-row blocks.
+  static_assert(HP == 1 || HP == 2 || HP == 4, "heads per workgroup");
+  constexpr int RPH = BM / HP;  // query rows per head
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int i32 = lane & 31;
   const int g = lane >> 5;
-  const int group = wave >> 2;                      // 0: M on even phases, 1: M on odd phases
-  const int row_block = 2 * (wave & 3) + group;     // the SIMD's two waves own adjacent blocks
+  const int group = wave >> 2;                          // 0: M on even phases, 1: M on odd phases
+  const int si = wave & 3;                              // SIMD
+  const int row_block = 2 * (si % (4 / HP)) + group;    // 32-row block within the head's rows
+  const int hsub = si / (4 / HP);                       // head within the workgroup
 
-  // ---- work item: (q-tile, batch, query head) ------------------------------
+  // ---- work item: (q-tile, batch, HP query heads) -----------------------------
+  const int gh = p.group / HP;  // head packs per KV head
   int qt_seq, b, hq;
   if (p.xcd_remap) {
     const int xcd = blockIdx.x & 7;
     const int j = blockIdx.x >> 3;
-    const int per_qt = (p.B * p.Hkv / 8) * p.group;
+    const int per_qt = (p.B * p.Hkv / 8) * gh;
     qt_seq = j / per_qt;
     const int rem = j - qt_seq * per_qt;
-    const int pair = (rem / p.group) * 8 + xcd;
-    const int gq = rem - (rem / p.group) * p.group;
+    const int pair = (rem / gh) * 8 + xcd;
+    const int gq = rem - (rem / gh) * gh;
     b = pair / p.Hkv;
-    hq = (pair - b * p.Hkv) * p.group + gq;
+    hq = (pair - b * p.Hkv) * p.group + gq * HP + hsub;
   } else {
-    const int BH = p.B * p.Hq;
+    const int BH = p.B * (p.Hq / HP);
     qt_seq = blockIdx.x / BH;
     const int rem = blockIdx.x - qt_seq * BH;
-    b = rem / p.Hq;
-    hq = rem - b * p.Hq;
+    b = rem / (p.Hq / HP);
+    hq = (rem - b * (p.Hq / HP)) * HP + hsub;
   }
   const int qt = CAUSAL ? (p.n_qtiles - 1 - qt_seq) : qt_seq;
   const int hk = hq / p.group;
 
-  const int q0 = qt * BM;
+  const int q0 = qt * RPH;
   const int qw = q0 + row_block * 32;
   const int qi = qw + i32;
 
@@ -161,7 +176,7 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   const int k_tile = BN * p.k_ss, v_tile = BN * p.v_ss;
   const int k_limit = (p.Sk - 1) * p.k_ss + RB, v_limit = (p.Sk - 1) * p.v_ss + RB;
 
-  const int kv_end = CAUSAL ? min(p.Sk, q0 + BM + p.causal_off) : p.Sk;
+  const int kv_end = CAUSAL ? min(p.Sk, q0 + RPH + p.causal_off) : p.Sk;
   const int n_tiles = (kv_end + BN - 1) / BN;  // tiles any wave of the workgroup needs
   const bool wave_active = qw < p.Sq;
   const int T = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / BN + 1) : n_tiles);
@@ -260,6 +275,19 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
     }
   };
 
+  // M(0): no probabilities yet, so only S(0) = K(0).Q^T.
+  auto m_first = [&](const unsigned char* kl) {
+    if (T == 0) return;
+    qk_part(kl);
+    constexpr int NQK = KB * QS;
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LA < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
   // p = exp2(c S) for the whole tile: the P^T operand of the next M phase
   // (rounded to bf16) and this lane's partial row sum (fp32, unrounded).
   auto exp_tile = [&]() -> float {
@@ -334,12 +362,8 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
     if (n < n_tiles) dma_tile(vbase, v_tile, n, v_limit, vdma_off, v_dst + dma_dst);
   };
 
-  // ---- prologue: K(0) into slot 0 and V slot 1 zeroed (read by M(0)),
-  // published before phase 0 ----------------------------------------------------
+  // ---- prologue: K(0) into slot 0, published before phase 0 ------------------
   if (n_tiles > 0) dma_tile(kbase, k_tile, 0, k_limit, kdma_off, k_lds0 + dma_dst);
-#pragma unroll
-  for (int t = 0; t < TILE / (16 * 64 * WAVES); ++t)
-    *(u32x4*)(v_lds1 + 16 * (tid + 64 * WAVES * t)) = u32x4{0, 0, 0, 0};
   barrier_after<kWaitVm0Lgkm0>();
 
   // ---- global phases ----------------------------------------------------------
@@ -351,14 +375,17 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   //   phase 4k+1 :                            | A: V(2k)            | B: M(2k)   [k0, v1]
   //   phase 4k+2 : DMA K(2k+2)->k0, V(2k+1)->v1 | A: M(2k+1) [k1, v0] | B: V(2k)
   //   phase 4k+3 :                            | A: V(2k+1)          | B: M(2k+1) [k1, v0]
-  // Each group runs its own loop of four-phase trips, so a score tile never
-  // crosses a trip; both loops execute n_trips * 4 + 2 barriers.
+  // M(0) has no P.V and stands before each group's loop, which is rotated to
+  // start one phase later. Each group runs its own loop of four-phase trips,
+  // so a score tile never crosses a trip; both groups execute n_trips * 4 + 2
+  // barriers after the prologue's (group B skips its last, which would follow
+  // M(2 n_trips), a phase past every wave's last tile).
   const int n_trips = (n_tiles + 2) / 2;  // covers M(0..n_tiles) and V(0..n_tiles-1)
   if (group == 0) {
+    m_first(k_lds0);
+    dma_phase(0, k_lds1, v_lds0);
+    barrier_after<kWaitLgkm0>();
     for (int k = 0; k < n_trips; ++k) {
-      m_phase(2 * k, k_lds0, v_lds1);
-      dma_phase(2 * k, k_lds1, v_lds0);
-      barrier_after<kWaitLgkm0>();
       v_phase(2 * k);
       barrier_after<kWaitVm0Lgkm0>();
       m_phase(2 * k + 1, k_lds1, v_lds0);
@@ -366,15 +393,16 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
       barrier_after<kWaitLgkm0>();
       v_phase(2 * k + 1);
       barrier_after<kWaitVm0Lgkm0>();
+      m_phase(2 * k + 2, k_lds0, v_lds1);
+      dma_phase(2 * k + 2, k_lds1, v_lds0);
+      barrier_after<kWaitLgkm0>();
     }
-    dma_phase(2 * n_trips, k_lds1, v_lds0);  // phase 4 n_trips: nothing left to compute
-    barrier_after<kWaitLgkm0>();
   } else {
     dma_phase(0, k_lds1, v_lds0);  // phase 0: no score tile yet
     barrier_after<kWaitLgkm0>();
+    m_first(k_lds0);
+    barrier_after<kWaitVm0Lgkm0>();
     for (int k = 0; k < n_trips; ++k) {
-      m_phase(2 * k, k_lds0, v_lds1);
-      barrier_after<kWaitVm0Lgkm0>();
       dma_phase(2 * k + 1, k_lds0, v_lds1);
       v_phase(2 * k);
       barrier_after<kWaitLgkm0>();
@@ -383,6 +411,8 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
       dma_phase(2 * k + 2, k_lds1, v_lds0);
       v_phase(2 * k + 1);
       barrier_after<kWaitLgkm0>();
+      m_phase(2 * k + 2, k_lds0, v_lds1);
+      if (k + 1 < n_trips) barrier_after<kWaitVm0Lgkm0>();  // M(2 n_trips) is past every T
     }
   }
 
@@ -424,11 +454,20 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
 int bf16_pp_block_m() { return pp::BM; }
 
 hipError_t launch_attn_bf16_pp(const AttnParams& p, bool causal, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  // Under the causal mask the waves of a 256-row q-tile need different numbers
+  // of key tiles and the phase barriers make every wave wait for the longest.
+  // When four (two) query heads share a KV head, a workgroup instead takes 64
+  // (128) rows of each of four (two) heads: the waves read the same K/V tiles
+  // and need the same number of them (two numbers, one apart, with two heads).
+  const int hp = !causal ? 1 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
   AttnParams arg = p;
+  arg.n_qtiles = (p.Sq + pp::BM / hp - 1) / (pp::BM / hp);
+  const unsigned grid = (unsigned)arg.n_qtiles * (unsigned)p.B * (unsigned)(p.Hq / hp);
   void* args[] = {&arg};
-  const void* fn = causal ? (const void*)&pp::attn_fwd_bf16_pp_kernel<true>
-                          : (const void*)&pp::attn_fwd_bf16_pp_kernel<false>;
+  const void* fn = !causal   ? (const void*)&pp::attn_fwd_bf16_pp_kernel<false, 1>
+                   : hp == 4 ? (const void*)&pp::attn_fwd_bf16_pp_kernel<true, 4>
+                   : hp == 2 ? (const void*)&pp::attn_fwd_bf16_pp_kernel<true, 2>
+                             : (const void*)&pp::attn_fwd_bf16_pp_kernel<true, 1>;
   return hipLaunchKernel(fn, dim3(grid), dim3(pp::WAVES * 64), args, 0, stream);
 }
 

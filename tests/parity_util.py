@@ -26,8 +26,13 @@ TOL_LSE = {"f32": 1e-4, "bf16": 1e-4, "fp8": 1e-3}
 
 
 def kernel_block_m(w) -> int:
-    """Query rows per workgroup of the kernel the launcher picks for ``w``: the
-    d = 128 bf16 and fp8 kernels take 256-row tiles, the others 128."""
+    """Query rows per head of one workgroup of the kernel the launcher picks for
+    ``w``: the d = 128 bf16 and fp8 kernels take 256-row tiles, the others 128;
+    the causal d = 128 bf16 kernel packs 4 (2) query heads of one KV head into
+    a workgroup when the group size divides by 4 (2), 64 (128) rows each."""
+    if w.d == 128 and w.dtype == "bf16" and w.causal:
+        G = w.Hq // w.Hkv
+        return 64 if G % 4 == 0 else 128 if G % 2 == 0 else 256
     return 256 if (w.d == 128 and w.dtype in ("bf16", "fp8")) else 128
 
 

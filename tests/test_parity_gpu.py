@@ -22,7 +22,7 @@ from parity_util import TOL_LSE, TOL_O, check_full, check_sampled, log, run_gpu,
 pytestmark = pytest.mark.gpu
 
 TAIL_S = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 196, 255, 257]
-HEADS = [(8, 8), (8, 2), (8, 1)]
+HEADS = [(8, 8), (8, 4), (8, 2), (8, 1)]
 
 
 def _run_full(w, want_lse=True):
@@ -100,9 +100,11 @@ def test_causal_queries_are_the_last_positions(gpu, dtype, d, Sq, Sk):
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_batch_and_heads_mapping(gpu, d):
-    """Several batches and GQA groups at once, causal, lse on."""
+    """Several batches and GQA groups at once, causal, lse on: groups of 4 and 2 query heads
+    with the XCD-ordered work items (B * Hkv divisible by 8) and without."""
     for dtype in ("f32", "bf16", "fp8"):
-        _run_full(sdpa_inputs.custom(3, 12, 3, 200, 200, d, dtype, True, seed=55))
+        for B, Hq, Hkv, S in ((3, 12, 3, 200), (2, 16, 4, 333), (2, 16, 8, 333), (4, 12, 2, 129)):
+            _run_full(sdpa_inputs.custom(B, Hq, Hkv, S, S, d, dtype, True, seed=55 + Hq + Hkv))
 
 
 # ------------------------------------------------------------- golden fixtures
