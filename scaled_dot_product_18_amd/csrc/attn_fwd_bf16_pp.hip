@@ -36,6 +36,11 @@
 // four phases so that every slot is a fixed LDS object and the compiler can
 // see that a read never touches the slot being filled.
 //
+// Q: each wave loads its 32 rows once, as whole rows through the same DMA
+// into a staging buffer (1 KB of four rows per load; a fragment-shaped load
+// from HBM would touch 32 rows per instruction), and reads its Q fragment from
+// there with the K tile's swizzle.
+//
 // Lane layout (unchanged from the four-wave kernel): S^T and O^T are computed
 // transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one query
 // column; the bf16-rounded score accumulator is directly the P^T operand; V^T
@@ -121,10 +126,13 @@ __device__ __forceinline__ void barrier_after() {
 template <bool CAUSAL, int HP>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_pp_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[TILE];
+  // The larger alignment places the K/V slots first: the operand reads reach
+  // them through 16-bit immediate offsets.
+  __shared__ __attribute__((aligned(4096))) unsigned char k_lds0[TILE];
+  __shared__ __attribute__((aligned(4096))) unsigned char k_lds1[TILE];
+  __shared__ __attribute__((aligned(4096))) unsigned char v_lds0[TILE];
+  __shared__ __attribute__((aligned(4096))) unsigned char v_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char q_stage[WAVES * 32 * RB];
 
   // HP query heads of one KV head share the workgroup, BM / HP rows each: SIMD
   // si serves head si / (4 / HP), and its two waves own adjacent 32-row blocks.
@@ -193,12 +201,22 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   }
   const int dma_dst = 1024 * DMA * wave;
 
-  // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8)
+  // ---- Q rows of this wave HBM -> LDS as whole rows (1 KB per load, four
+  // rows), 16-byte chunks swizzled as in a K tile; rows at or past Sq load as
+  // zeros. The fragments are read from there after the prologue's barrier.
   const float c = p.qk_scale_log2;
-  u32x4 qf[QS];
+  unsigned char* q_mine = q_stage + wave * (32 * RB);
+  if (wave_active) {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qbase + (size_t)qw * p.q_ss), (short)0, (p.Sq - qw - 1) * p.q_ss + RB, kBufferConfig);
 #pragma unroll
-  for (int s = 0; s < QS; ++s)
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+    for (int t = 0; t < 32 * RB / 1024; ++t) {
+      const int row = 4 * t + (lane >> 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(q_mine + 1024 * t), 16,
+                                               row * p.q_ss + 16 * ((lane & 15) ^ k_swizzle(row)), 0, 0, 0);
+    }
+  }
+  u32x4 qf[QS];
 
   int k_rd[QS];
 #pragma unroll
@@ -365,6 +383,9 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
   // ---- prologue: K(0) into slot 0, published before phase 0 ------------------
   if (n_tiles > 0) dma_tile(kbase, k_tile, 0, k_limit, kdma_off, k_lds0 + dma_dst);
   barrier_after<kWaitVm0Lgkm0>();
+  // Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8) of row i32.
+#pragma unroll
+  for (int s = 0; s < QS; ++s) qf[s] = *(const u32x4*)(q_mine + k_rd[s]);
 
   // ---- global phases ----------------------------------------------------------
   // Global phase p ends with a barrier that waits for this wave's LDS reads
