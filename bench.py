@@ -37,6 +37,8 @@ Other modes:
     --sweep                  the codelab's own benchmark shapes (one JSON line per shape, see sweep_shapes)
     --eager                  time forward steps as K separate calls with events around each (default: one HIP
                              graph of the K launches, replayed once)
+    --mfma-peak              the matrix-core ceiling: bf16, fp8 and fp32 MFMA streams on register operands, one and
+                             two waves per SIMD (libmfmapeak.so), one JSON line per case
 """
 
 from __future__ import annotations
@@ -296,6 +298,63 @@ def sweep_shapes():
     return out
 
 
+MFMA_KINDS = [  # (kind, instruction, FLOP per instruction, published dense peak TFLOP/s)
+    (0, "v_mfma_f32_32x32x16_bf16", 32768, PEAK_TFLOPS["bf16"]),
+    (1, "v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3)", 131072, PEAK_TFLOPS["fp8"]),
+    (2, "v_mfma_f32_32x32x2_f32", 4096, PEAK_TFLOPS["f32"]),
+]
+
+
+def run_mfma_peak(warm_seconds: float = 1.0, repeats: int = 5) -> int:
+    """The matrix-core ceiling the attention kernels are measured against: every
+    wave streams MFMAs on register operands (libmfmapeak.so, built beside the
+    attention library), one and two waves per SIMD. One JSON line per case:
+    achieved TFLOP/s (median of `repeats` launches of about 20 ms, after
+    `warm_seconds` of launches) and its fraction of the published dense peak."""
+    import ctypes
+    import torch
+    from scaled_dot_product_18_amd import build as _build
+    if not os.path.exists(_build.PEAK_LIB_PATH):
+        raise SystemExit(f"{_build.PEAK_LIB_PATH} is missing: build first (python -m scaled_dot_product_18_amd.build)")
+    lib = ctypes.CDLL(_build.PEAK_LIB_PATH)
+    lib.mfma_peak_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_peak_launch.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    for kind, instr, flop, peak in MFMA_KINDS:
+        for wps in (1, 2):
+            blocks = cus * wps
+            sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+
+            def launch(iters):
+                rc = lib.mfma_peak_launch(kind, blocks, iters, sink.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mfma_peak_launch: status {rc}")
+
+            def timed(iters):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch(iters)
+                e1.record(stream)
+                e1.synchronize()
+                return e0.elapsed_time(e1) * 1e-3
+
+            iters = 1000
+            for _ in range(3):  # about 20 ms per launch, once the clock has left its idle state
+                iters = max(1000, int(iters * 0.02 / max(timed(iters), 1e-6)))
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < warm_seconds:
+                timed(iters)
+            ts = sorted(timed(iters) for _ in range(repeats))
+            t = ts[len(ts) // 2]
+            total = blocks * 4 * iters * 8 * flop
+            print(json.dumps({"mfma_peak": instr, "waves_per_simd": wps, "workgroups": blocks, "iters": iters,
+                              "launch_ms": round(t * 1e3, 3), "tflops": round(total / t / 1e12, 1),
+                              "published_peak_tflops": peak, "frac_of_published": round(total / t / 1e12 / peak, 4)}),
+                  flush=True)
+    return 0
+
+
 def run_sweep(warmup: int = 2, repeats: int = 20) -> int:
     """Time every sweep shape like the codelab's helper (warm-up calls, then the
     median of the timed calls, each with HIP events on the launch stream around
@@ -366,6 +425,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="measure the matrix-core ceiling (MFMA streams on register operands) instead")
     ap.add_argument("--eager", action="store_true")
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="after --warmup calls, keep launching for this long before timing")
@@ -387,6 +448,8 @@ def main() -> int:
         return 0
     if args.sweep:
         return run_sweep()
+    if args.mfma_peak:
+        return run_mfma_peak()
 
     import sdpa_inputs
     import scaled_dot_product_18_amd as sdpa

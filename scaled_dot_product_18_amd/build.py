@@ -2,7 +2,9 @@
 
     python -m scaled_dot_product_18_amd.build [--verbose]
 
-Produces ``scaled_dot_product_18_amd/libsdpa18.so`` in-tree. Every
+Produces ``scaled_dot_product_18_amd/libsdpa18.so`` in-tree, and beside it
+``libmfmapeak.so``, the matrix-core throughput microbenchmark that
+``bench.py --mfma-peak`` runs (not part of the attention library). Every
 translation unit is compiled with packed fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass
 warns that it does not know the feature, which is harmless.
@@ -24,6 +26,8 @@ LIB_NAME = "libsdpa18.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
+PEAK_SOURCE = "mfma_peak.hip"
+PEAK_LIB_PATH = os.path.join(PKG_DIR, "libmfmapeak.so")
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_pp.hip", "attn_fwd_fp8_pp.hip", "attn_fwd_mfma.hip",
            "attn_fwd_f32.hip", "attn_fwd_splitkv.hip", "attn_bwd.hip", "attn_bwd_f32.hip"]
 
@@ -63,16 +67,20 @@ def build(verbose: bool = False, out_dir: str | None = None) -> str:
             print(err, file=sys.stderr)
         return obj
 
+    def link(objs, path):
+        tmp = path + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
+        os.replace(tmp, path)
+        if verbose:
+            print(f"built {path}")
+
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print(f"built {LIB_PATH}")
+        objs = list(ex.map(compile_one, SOURCES + [PEAK_SOURCE]))
+    link(objs[:-1], LIB_PATH)
+    link(objs[-1:], PEAK_LIB_PATH)
     return LIB_PATH
 
 

@@ -297,3 +297,13 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+(oracle|sdpa_inputs)\b", text, flags=re.M), fn
                 assert "oracle/" not in text, fn
+
+
+def test_mfma_peak_library_is_built_apart_from_the_boundary():
+    """The matrix-core microbenchmark (bench.py --mfma-peak) lives in its own library: it exports
+    its launcher, and the attention library does not."""
+    from scaled_dot_product_18_amd import _lib, build
+    if not os.path.exists(build.PEAK_LIB_PATH):
+        pytest.fail(f"{build.PEAK_LIB_PATH} not built: run __graft_entry__.build()")
+    assert hasattr(ctypes.CDLL(build.PEAK_LIB_PATH), "mfma_peak_launch")
+    assert not hasattr(ctypes.CDLL(_lib.LIB_PATH), "mfma_peak_launch")
