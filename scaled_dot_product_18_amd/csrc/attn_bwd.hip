@@ -51,15 +51,20 @@ struct Cfg {
 };
 
 // Chunk swizzles. Tiles read only row-wise (16 lanes at 16 rows, one chunk)
-// use row_swz; tiles also read through the transposing read (4 consecutive
-// rows, 32 bytes each) use tr_swz, which keeps those free of bank conflicts.
+// use row_swz. Tiles also read through the transposing read (lanes 0-31: 4
+// consecutive rows, 64 bytes each) use dual_swz, which keeps both kinds free
+// of bank conflicts: at d = 128 the row's two low bits pick the chunk's two
+// high bits (4 consecutive rows cover the four 64-byte quarters of the banks)
+// and its next two bits the chunk's low bits (16 consecutive rows cover all 16
+// chunks); at d = 64, where two 128-byte rows share the banks, bit 1 of the
+// row picks the chunk's high bit and bits 2-3 its low bits.
 template <int D>
 __device__ __forceinline__ int row_swz(int row) {
   return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 template <int D>
-__device__ __forceinline__ int tr_swz(int row) {
-  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
+__device__ __forceinline__ int dual_swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 // This wave's DMA loads of tile t of a row-major [rows, D] bf16 array, HBM ->
@@ -77,17 +82,18 @@ __device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_byt
 
 // Offsets of the transposing reads that form a 32 (dim) x 16 (row) A operand
 // from a row-major tile: in each 16-lane group lane J reads 4 dims
-// [dbase + 4(J%4), +4) of row (row_base + J/4); the lo read covers rows
-// 16kc + 4g + J/4, the hi read the same rows + 8. Element e of the operand then
-// pairs with row 16kc + 8(e/4) + 4g + e%4, the row order of the packed
-// accumulator operands below.
+// [dbase + 4(J%4), +4) of row (row_base + J/4); the lo read (hi = 0) covers
+// rows 16kc + 4g + J/4, the hi read (hi = 1) the same rows + 8, each with its
+// own row's swizzle (row_base is a multiple of 16, which the swizzle ignores).
+// Element e of the operand then pairs with row 16kc + 8(e/4) + 4g + e%4, the
+// row order of the packed accumulator operands below.
 template <int D>
-__device__ __forceinline__ int tr_offset(int lane, int db) {
+__device__ __forceinline__ int tr_offset(int lane, int db, int hi) {
   const int J = lane & 15;
   const int g = lane >> 5;
-  const int r = 4 * g + (J >> 2);
+  const int r = 4 * g + (J >> 2) + 8 * hi;
   const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
-  return r * (2 * D) + 16 * ((d >> 3) ^ tr_swz<D>(r)) + 2 * (d & 7);
+  return r * (2 * D) + 16 * ((d >> 3) ^ dual_swz<D>(r)) + 2 * (d & 7);
 }
 
 // 64 consecutive fp32 per-row statistics of tile t (one per query of the tile)
@@ -98,9 +104,9 @@ __device__ __forceinline__ void dma_stat(const float* base, int t, int total_byt
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, 4 * lane, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* p, int rb) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * rb));
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* p, int lo_off, int hi_off) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + lo_off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi_off));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -207,7 +213,7 @@ void attn_bwd_dq_kernel(const BwdParams p) {
   for (int i = 0; i < C::DMA; ++i) {
     const int r = (64 * (C::DMA * wave + i) + lane) / C::CH;
     const int pc = lane % C::CH;
-    kdma[i] = r * C::RB + 16 * (pc ^ tr_swz<D>(r));   // K: row reads and transposing reads
+    kdma[i] = r * C::RB + 16 * (pc ^ dual_swz<D>(r));   // K: row reads and transposing reads
     vdma[i] = r * C::RB + 16 * (pc ^ row_swz<D>(r));  // V: row reads
   }
 
@@ -225,14 +231,17 @@ void attn_bwd_dq_kernel(const BwdParams p) {
   const float lse2 = qi < p.Sq ? p.lse[qo_row0 + qi] * kLog2e : 0.f;
   const float dlt = qi < p.Sq ? p.delta[qo_row0 + qi] : 0.f;
 
-  int k_rd[C::QS], v_rd[C::QS], kt_rd[C::DB];
+  int k_rd[C::QS], v_rd[C::QS], kt_lo[C::DB], kt_hi[C::DB];
 #pragma unroll
   for (int s = 0; s < C::QS; ++s) {
-    k_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ tr_swz<D>(i32));
+    k_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ dual_swz<D>(i32));
     v_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ row_swz<D>(i32));
   }
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) kt_rd[db] = tr_offset<D>(lane, db);
+  for (int db = 0; db < C::DB; ++db) {
+    kt_lo[db] = tr_offset<D>(lane, db, 0);
+    kt_hi[db] = tr_offset<D>(lane, db, 1);
+  }
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -276,13 +285,22 @@ void attn_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) dsf[2 * kb + j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T. Its own scheduling region: the two transposing reads
+    // of each operand run LA MFMAs ahead of the matrix core.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kl + 16 * kc * C::RB + kt_rd[db], C::RB),
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kl + 16 * kc * C::RB, kt_lo[db], kt_hi[db]),
                                                           __builtin_bit_cast(bf16x8, dsf[kc]), acc[db], 0, 0, 0);
+    constexpr int NUP = C::DB * 4, LA = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+    for (int i = 0; i < NUP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LA < NUP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
   const int kv_bytes = p.Sk * C::RB;
@@ -369,13 +387,16 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i) {
     const int r = (64 * (C::DMA * wave + i) + lane) / C::CH;
-    qdma[i] = r * C::RB + 16 * ((lane % C::CH) ^ tr_swz<D>(r));  // Q and dO: row and transposing reads
+    qdma[i] = r * C::RB + 16 * ((lane % C::CH) ^ dual_swz<D>(r));  // Q and dO: row and transposing reads
   }
-  int q_rd[C::QS], t_rd[C::DB];
+  int q_rd[C::QS], t_lo[C::DB], t_hi[C::DB];
 #pragma unroll
-  for (int s = 0; s < C::QS; ++s) q_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ tr_swz<D>(i32));
+  for (int s = 0; s < C::QS; ++s) q_rd[s] = i32 * C::RB + 16 * ((2 * s + g) ^ dual_swz<D>(i32));
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) t_rd[db] = tr_offset<D>(lane, db);
+  for (int db = 0; db < C::DB; ++db) {
+    t_lo[db] = tr_offset<D>(lane, db, 0);
+    t_hi[db] = tr_offset<D>(lane, db, 1);
+  }
 
   f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
@@ -449,19 +470,28 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
           dsf[qb][j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
         }
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS
+    // dV^T += dO^T P,  dK^T += Q^T dS. Its own scheduling region: the two
+    // transposing reads of each operand run LA MFMAs ahead of the matrix core.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const int base = (32 * qb + 16 * kc) * C::RB + t_rd[db];
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ol + base, C::RB),
+          const int base = (32 * qb + 16 * kc) * C::RB;
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ol + base, t_lo[db], t_hi[db]),
                                                            __builtin_bit_cast(bf16x8, pf[qb][kc]), dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ql + base, C::RB),
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ql + base, t_lo[db], t_hi[db]),
                                                            __builtin_bit_cast(bf16x8, dsf[qb][kc]), dk[db], 0, 0, 0);
         }
+    constexpr int NUP = NB * C::DB * 2 * 2, LA = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+    for (int i = 0; i < NUP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LA < NUP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
   // Whether any query of tile t sees a key of this wave (always, without the mask).
