@@ -337,6 +337,12 @@ void attn_bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK, dV
+// One wave per SIMD (the wave's K and V rows and its dK, dV accumulators take
+// most of the register file), so the wave overlaps its own vector and matrix
+// work: query tiles are software-pipelined, and one step runs the P/dS
+// arithmetic of tile t (VALU) beside the S/dP products of tile t+1 (matrix
+// core), then the dV/dK products of tile t. Q, dO and their statistics go
+// through three LDS buffers: t, t+1 and the load of t+2 in flight.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1)))
 void attn_bwd_dkdv_kernel(const BwdParams p) {
@@ -345,9 +351,12 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[C::TILE];  // dO
   __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[C::TILE];
-  // lse2 and delta of the tile's 64 queries, streamed with the tile
+  __shared__ __attribute__((aligned(1024))) unsigned char q_lds2[C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char o_lds2[C::TILE];
+  // lse2 and delta of a tile's 64 queries, streamed with the tile
   __shared__ __attribute__((aligned(256))) float st_lds0[2 * C::BT];
   __shared__ __attribute__((aligned(256))) float st_lds1[2 * C::BT];
+  __shared__ __attribute__((aligned(256))) float st_lds2[2 * C::BT];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -406,132 +415,183 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   }
   const float c = p.qk_scale_log2;
   const int off = p.causal_off;
-  // Queries that see a key of this workgroup: i >= k0 - off (all of them without the mask).
+  // Query tiles from the first one that sees a key of this workgroup (i >= k0 - off; all without the mask).
   const int t_first = CAUSAL ? max(0, k0 - off) / C::BT : 0;
   const int n_qt = (p.Sq + C::BT - 1) / C::BT;
 
-  size_t qo_row0 = 0;
-  // One 64-query tile in three stages, so the matrix core has independent work
-  // while the vector unit turns scores into P and dS: S and dP of both 32-query
-  // blocks, then P and dS of both, then the dV and dK updates of both. A block
-  // of queries past Sq, or that sees none of this wave's keys under the mask,
-  // is masked to zero rather than skipped, keeping the stages branch-free.
-  auto compute_tile = [&](int t, const unsigned char* ql, const unsigned char* ol, const float* stl) {
-    constexpr int NB = 2;
-    // S = Q K^T, dP = dO V^T: lane = key kj, register r on half g <-> query qb0 + 8(r/4) + 4g + r%4
-    f32x16 s[NB], dp[NB];
+  // The work of one 64-query tile t for this wave's 32 keys, in two 32-query
+  // blocks qb (lane = key kj; register r on half g <-> query 32qb + 8(r/4) + 4g + r%4):
+  //   A(qb): S = Q K^T and dP = dO V^T, 2 D/16 MFMAs with a row read of Q or dO each;
+  //   B(qb): P = exp2(c S - lse2) under the mask, dS = P (dP - delta), rounded
+  //          to bf16 as B operands, four groups of 4 elements (VALU);
+  //   C(qb): dV^T += dO^T P, dK^T += Q^T dS, 2 D/16 MFMAs with two transposing reads each.
+  // One pipeline step for tile t runs four parts of 4-MFMA sub-chunks (four
+  // per part at d = 128, two at d = 64), each sub-chunk beside its share of
+  // vector work where there is one, with the next sub-chunk's operands read
+  // ahead; fences keep the compiler from regrouping them:
+  //    part 0  A(t, 1)   | B(t, 0)        part 2  A(t+1, 0) | -
+  //    part 1  C(t, 0)   | B(t, 1)        part 3  C(t, 1)   | -
+  // A(t+1, 0) reads tile t+1's buffers, so they are loaded one step ahead
+  // (three buffer sets: t, t+1, and t+2 in flight). Past the last tile it
+  // runs on a stale buffer and its results are never used.
+  // Query rows past Sq need no mask: their Q, dO, lse2 and delta load as
+  // zeros, so dS = 0 and they add nothing to dV = P^T dO; keys past Sk are
+  // never stored, and each key's gradients stay in its own lane.
+  constexpr int NB = 2;
+  f32x16 s[NB], dp[NB];
+  u32x4 pf[NB][2], dsf[NB][2];
+  float pr[NB][16], ds[NB][16];
+  // A MFMA i of block qb (0 <= i < NP): S for i < QS, dP after, over dims st = i % QS.
+  constexpr int NP = 2 * C::QS;  // MFMAs of one stage for one block (A and C alike: 4 DB = 2 QS)
+  static_assert(NP == 4 * C::DB && NP % 4 == 0, "stage sizes");
+  auto a_operand = [&](int i, const unsigned char* ql, const unsigned char* ol, int qb) {
+    return *(const u32x4*)((i >= C::QS ? ol : ql) + 32 * qb * C::RB + q_rd[i % C::QS]);
+  };
+  auto a_mfma = [&](int i, int qb, u32x4 a) {
+    const int st = i % C::QS;
+    if (i < C::QS)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, kf[st]),
+                                                      st == 0 ? f32x16{} : s[qb], 0, 0, 0);
+    else
+      dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, vf[st]),
+                                                       st == 0 ? f32x16{} : dp[qb], 0, 0, 0);
+  };
+  // C MFMA i of block qb: db = i / 4, kc = (i / 2) % 2; even i: dV (dO^T), odd i: dK (Q^T)
+  auto c_operand = [&](int i, const unsigned char* ql, const unsigned char* ol, int qb) {
+    const int db = i >> 2, kc = (i >> 1) & 1;
+    return tr_operand(((i & 1) ? ql : ol) + (32 * qb + 16 * kc) * C::RB, t_lo[db], t_hi[db]);
+  };
+  auto c_mfma = [&](int i, int qb, bf16x8 a) {
+    const int db = i >> 2, kc = (i >> 1) & 1;
+    if ((i & 1) == 0)
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[qb][kc]), dv[db], 0, 0, 0);
+    else
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, dsf[qb][kc]), dk[db], 0, 0, 0);
+  };
+  // B group m of block qb with its statistics (lse2, delta of queries 32qb + 8m + 4g + 0..3).
+  auto b_group = [&](int t, int qb, int m, f32x4 l2, f32x4 dl) {
+    const int vis = t * C::BT + off - kj + 4 * g;  // query 32qb+8m+4g+e sees kj iff vis + 32qb + 8m + e >= 0
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < C::QS; ++st) {
-        const u32x4 a = *(const u32x4*)(ql + 32 * qb * C::RB + q_rd[st]);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, kf[st]), s[qb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int st = 0; st < C::QS; ++st) {
-        const u32x4 a = *(const u32x4*)(ol + 32 * qb * C::RB + q_rd[st]);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                         __builtin_bit_cast(bf16x8, vf[st]), dp[qb], 0, 0, 0);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * m + e;
+      float x = exp2_fast(__builtin_fmaf(s[qb][r], c, -l2[e]));
+      if (CAUSAL) x = (vis >= -(32 * qb + 8 * m + e)) ? x : 0.f;
+      pr[qb][r] = x;
+      ds[qb][r] = x * (dp[qb][r] - dl[e]);
     }
-    // P and dS operands: chunk kc, element e <-> query qb0 + 16kc + 8(e/4) + 4g + e%4
-    u32x4 pf[NB][2], dsf[NB][2];
+    if (m & 1) {
+      const int j = m >> 1;
 #pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      const int qb0 = t * C::BT + 32 * qb;
-      const bool edge = (CAUSAL && kw + 31 > qb0 + off) || qb0 + 32 > p.Sq || kw + 32 > p.Sk;
-      float pr[16], ds[16];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // lse2 / delta of queries qb0 + 8m + 4g + (0..3): one 16-byte LDS read each
-        const f32x4 l2 = *(const f32x4*)(stl + 32 * qb + 8 * m + 4 * g);
-        const f32x4 dl = *(const f32x4*)(stl + C::BT + 32 * qb + 8 * m + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * m + e;
-          float x = exp2_fast(__builtin_fmaf(s[qb][r], c, -l2[e]));
-          if (edge) {
-            const int qq = qb0 + 8 * m + 4 * g + e;
-            const bool ok = qq < p.Sq && kj < p.Sk && (!CAUSAL || kj <= qq + off);
-            x = ok ? x : 0.f;
-          }
-          pr[r] = x;
-          ds[r] = x * (dp[qb][r] - dl[e]);
-        }
+      for (int e2 = 0; e2 < 4; ++e2) {
+        pf[qb][j][e2] = pack_bf16x2(pr[qb][8 * j + 2 * e2], pr[qb][8 * j + 2 * e2 + 1]);
+        dsf[qb][j][e2] = pack_bf16x2(ds[qb][8 * j + 2 * e2], ds[qb][8 * j + 2 * e2 + 1]);
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          pf[qb][j][e2] = pack_bf16x2(pr[8 * j + 2 * e2], pr[8 * j + 2 * e2 + 1]);
-          dsf[qb][j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
-        }
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS. Its own scheduling region: the two
-    // transposing reads of each operand run LA MFMAs ahead of the matrix core.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const int base = (32 * qb + 16 * kc) * C::RB;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ol + base, t_lo[db], t_hi[db]),
-                                                           __builtin_bit_cast(bf16x8, pf[qb][kc]), dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ql + base, t_lo[db], t_hi[db]),
-                                                           __builtin_bit_cast(bf16x8, dsf[qb][kc]), dk[db], 0, 0, 0);
-        }
-    constexpr int NUP = NB * C::DB * 2 * 2, LA = 4;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
-#pragma unroll
-    for (int i = 0; i < NUP; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + LA < NUP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
+  auto stat = [&](const float* stl, int qb, int m, int which) {
+    return *(const f32x4*)(stl + which * C::BT + 32 * qb + 8 * m + 4 * g);
+  };
 
-  // Whether any query of tile t sees a key of this wave (always, without the mask).
-  auto sees = [&](int t) { return !CAUSAL || t * C::BT + C::BT - 1 + off >= kw; };
   const int q_bytes = p.Sq * C::RB;
-  unsigned char* const qd0 = q_lds0 + 1024 * C::DMA * wave;
-  unsigned char* const od0 = o_lds0 + 1024 * C::DMA * wave;
-  unsigned char* const qd1 = q_lds1 + 1024 * C::DMA * wave;
-  unsigned char* const od1 = o_lds1 + 1024 * C::DMA * wave;
-  for (int gq = sp * heads; gq < (sp + 1) * heads; ++gq) {
-    const int hq = hk * p.group + gq;
-    qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
-    const unsigned char* qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
-    const unsigned char* obase = (const unsigned char*)p.dout + qo_row0 * C::RB;
-    // wave 0 streams lse2, wave 1 delta: 64 floats per tile, one 4-byte DMA per lane
-    const float* stat = (wave == 0 ? p.lse2 : p.delta) + qo_row0;
-    const int st_bytes = p.Sq * 4;
-    const int st_dst = wave == 0 ? 0 : 4 * C::BT;
-    if (t_first < n_qt) {
-      dma_tile<C::DMA>(qbase, C::TILE, t_first, q_bytes, qdma, qd0);
-      dma_tile<C::DMA>(obase, C::TILE, t_first, q_bytes, qdma, od0);
-      if (wave < 2) dma_stat(stat, t_first, st_bytes, lane, (unsigned char*)st_lds0 + st_dst);
+  const int st_bytes = p.Sq * 4;
+  const int st_dst = wave == 0 ? 0 : 4 * C::BT;
+  const unsigned char *qbase = nullptr, *obase = nullptr;
+  const float* stat_src = nullptr;
+  // Tile t's Q, dO and (waves 0 and 1: lse2, delta) statistics into one buffer set.
+  auto load = [&](int t, unsigned char* ql, unsigned char* ol, float* stl) {
+    dma_tile<C::DMA>(qbase, C::TILE, t, q_bytes, qdma, ql + 1024 * C::DMA * wave);
+    dma_tile<C::DMA>(obase, C::TILE, t, q_bytes, qdma, ol + 1024 * C::DMA * wave);
+    if (wave < 2) dma_stat(stat_src, t, st_bytes, lane, (unsigned char*)stl + st_dst);
+  };
+
+  // A step is 4 parts (0: A(t,1), 1: C(t,0), 2: A(t+1,0), 3: C(t,1)) of SUBS
+  // sub-chunks of 4 MFMAs; the first two parts also run GPS of the 4 B groups
+  // of their block per sub-chunk.
+  constexpr int SUBS = NP / 4, GPS = 4 / SUBS, NSUB = 4 * SUBS;
+  // Operands read ahead: A or C operands of the next sub-chunk, statistics of its B groups.
+  u32x4 aop[4];
+  bf16x8 cop[4];
+  f32x4 nl2[GPS], ndl[GPS];
+  auto fetch = [&](int k, const unsigned char* qc, const unsigned char* oc, const float* sc, const unsigned char* qn,
+                   const unsigned char* on) {
+    const int part = k / SUBS, i0 = 4 * (k % SUBS);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (part == 0) aop[u] = a_operand(i0 + u, qc, oc, 1);
+      if (part == 1) cop[u] = c_operand(i0 + u, qc, oc, 0);
+      if (part == 2) aop[u] = a_operand(i0 + u, qn, on, 0);
+      if (part == 3) cop[u] = c_operand(i0 + u, qc, oc, 1);
+    }
+    if (part < 2) {
+#pragma unroll
+      for (int h = 0; h < GPS; ++h) {
+        nl2[h] = stat(sc, part, GPS * (k % SUBS) + h, 0);
+        ndl[h] = stat(sc, part, GPS * (k % SUBS) + h, 1);
+      }
+    }
+  };
+  auto step = [&](int t, unsigned char* qc, unsigned char* oc, float* sc, unsigned char* qn, unsigned char* on,
+                  float* sn, unsigned char* qf_, unsigned char* of_, float* sf) {
+    if (t + 2 < n_qt) load(t + 2, qf_, of_, sf);
+#pragma unroll
+    for (int k = 0; k < NSUB; ++k) {
+      const int part = k / SUBS, i0 = 4 * (k % SUBS);
+      u32x4 a_cur[4];
+      bf16x8 c_cur[4];
+      f32x4 l2[GPS], dl[GPS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a_cur[u] = aop[u];
+        c_cur[u] = cop[u];
+      }
+#pragma unroll
+      for (int h = 0; h < GPS; ++h) {
+        l2[h] = nl2[h];
+        dl[h] = ndl[h];
+      }
+      // next sub-chunk's operands (sub-chunk NSUB is the next step's 0: tile t+1's A(1) and B(0) data)
+      if (k < NSUB - 1)
+        fetch(k + 1, qc, oc, sc, qn, on);
+      else
+        fetch(0, qn, on, sn, nullptr, nullptr);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (part == 0) a_mfma(i0 + u, 1, a_cur[u]);
+        if (part == 1) c_mfma(i0 + u, 0, c_cur[u]);
+        if (part == 2) a_mfma(i0 + u, 0, a_cur[u]);
+        if (part == 3) c_mfma(i0 + u, 1, c_cur[u]);
+      }
+      if (part < 2) {
+#pragma unroll
+        for (int h = 0; h < GPS; ++h) b_group(t, part, GPS * (k % SUBS) + h, l2[h], dl[h]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    for (int t = t_first; t < n_qt; t += 2) {
-      if (t + 1 < n_qt) {
-        dma_tile<C::DMA>(qbase, C::TILE, t + 1, q_bytes, qdma, qd1);
-        dma_tile<C::DMA>(obase, C::TILE, t + 1, q_bytes, qdma, od1);
-        if (wave < 2) dma_stat(stat, t + 1, st_bytes, lane, (unsigned char*)st_lds1 + st_dst);
-      }
-      if (wave_active && sees(t)) compute_tile(t, q_lds0, o_lds0, st_lds0);
-      __syncthreads();
-      if (t + 1 >= n_qt) break;
-      if (t + 2 < n_qt) {
-        dma_tile<C::DMA>(qbase, C::TILE, t + 2, q_bytes, qdma, qd0);
-        dma_tile<C::DMA>(obase, C::TILE, t + 2, q_bytes, qdma, od0);
-        if (wave < 2) dma_stat(stat, t + 2, st_bytes, lane, (unsigned char*)st_lds0 + st_dst);
-      }
-      if (wave_active && sees(t + 1)) compute_tile(t + 1, q_lds1, o_lds1, st_lds1);
-      __syncthreads();
+  };
+
+  for (int gq = sp * heads; gq < (sp + 1) * heads; ++gq) {
+    if (t_first >= n_qt) break;
+    const int hq = hk * p.group + gq;
+    const size_t qo_row0 = ((size_t)b * p.Hq + hq) * (size_t)p.Sq;
+    qbase = (const unsigned char*)p.q + qo_row0 * C::RB;
+    obase = (const unsigned char*)p.dout + qo_row0 * C::RB;
+    // wave 0 streams lse2, wave 1 delta: 64 floats per tile, one 4-byte DMA per lane
+    stat_src = (wave == 0 ? p.lse2 : p.delta) + qo_row0;
+    load(t_first, q_lds0, o_lds0, st_lds0);
+    if (t_first + 1 < n_qt) load(t_first + 1, q_lds1, o_lds1, st_lds1);
+    __syncthreads();
+    // A(t_first, 0), then the first step's operands
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a_mfma(i, 0, a_operand(i, q_lds0, o_lds0, 0));
+    fetch(0, q_lds0, o_lds0, st_lds0, nullptr, nullptr);
+    for (int t = t_first;;) {
+      step(t, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1, q_lds2, o_lds2, st_lds2);
+      if (++t >= n_qt) break;
+      step(t, q_lds1, o_lds1, st_lds1, q_lds2, o_lds2, st_lds2, q_lds0, o_lds0, st_lds0);
+      if (++t >= n_qt) break;
+      step(t, q_lds2, o_lds2, st_lds2, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
+      if (++t >= n_qt) break;
     }
   }
 
