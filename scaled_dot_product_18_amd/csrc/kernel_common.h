@@ -37,6 +37,7 @@ struct AttnParams {
   // pages' (B,T,N,H) layout has ss = N * d * element size, sh = d * element size.
   long long q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_ss, k_ss, v_ss, o_ss;
+  int p8_qtile = 0;  // fp8 d = 128 kernel: first q-tile whose P.V takes P rounded to e4m3
 };
 
 // First byte of head h of batch b of a strided [B,H,S,d] tensor.
