@@ -30,9 +30,11 @@
 //    stay e4m3 and go HBM -> LDS by DMA like K; the V^T operand comes from
 //    four transposing 8-bit reads (8 keys of one dimension each). P is kept
 //    as 2 P (the factor folds into the reference, so it costs nothing) and a
-//    lane's tile sum above 256 moves the reference, so no probability reaches
-//    the format's largest value 448; the row sums stay fp32 sums of the
-//    unrounded values. It runs for the q-tiles whose first query sees at least
+//    score that would make a stored 2 P exceed 256 moves the reference
+//    (tested on the lane's maximum score, before the exps), so no value
+//    reaches the format's largest value 448. The row sums stay fp32 sums of
+//    the unrounded values; the wave adds a tile's in its next M phase, beside
+//    the MFMAs. It runs for the q-tiles whose first query sees at least
 //    256 keys; workgroups of q-tiles that see fewer keys take the bf16 form.
 //
 // Memory path:
@@ -66,7 +68,6 @@ static_assert(BN * D == 16 * 64 * WAVES, "each lane stages 4 keys x 4 dims of V 
 
 constexpr int LA = 4;                       // MFMAs whose LDS operand reads are in flight ahead
 constexpr float kSumLimit = 4096.0f;        // see the bf16 ping-pong kernel
-constexpr float kSumLimitP8 = 256.0f;       // e4m3 P: every stored 2 P stays at or below 256 < 448
 constexpr int kBufferConfig = 0x00020000;   // word 3 of a raw buffer resource (gfx9 family)
 constexpr int kE8M0One = 127;               // E8M0 block scale 2^0
 constexpr int kWaitLgkm0 = 0xC07F;          // s_waitcnt lgkmcnt(0)
@@ -278,6 +279,19 @@ __device__ __forceinline__ void fp8_tile(const AttnParams& p) {
                                                           __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
       }
   };
+  // With e4m3 P the tile's unrounded probabilities wait in pk until the
+  // wave's next M phase adds them into l_run beside its MFMAs.
+  float pk[KB * 16];
+  auto add_pk = [&]() {
+    float lt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KB * 16; i += 2) {
+      lt[(i >> 1) & 3] += pk[i];
+      lt[(i >> 1) & 3] += pk[i + 1];
+    }
+    l_run += (lt[0] + lt[1]) + (lt[2] + lt[3]);
+  };
+
   auto pv_part8 = [&](const unsigned char* vl) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -306,6 +320,7 @@ __device__ __forceinline__ void fp8_tile(const AttnParams& p) {
   auto m_phase = [&](int m, const unsigned char* kl, const unsigned char* vl) {
     if (m > T) return;
     if constexpr (P8) {
+      add_pk();  // the row sum of tile m-1, beside the MFMAs
       pv_part8(vl);
       qk_part(kl);
       constexpr int NPV = DB, NMF = DB + KB * QS, LA8 = 2;  // 4 reads per P.V MFMA, 2 per Q.K^T MFMA
@@ -350,8 +365,9 @@ __device__ __forceinline__ void fp8_tile(const AttnParams& p) {
   };
 
   // p = exp2(c S) for the whole tile: the P^T operand (bf16) and this lane's
-  // partial row sum (fp32, unrounded). Registers 8j .. 8j+7 of block kb hold
-  // keys 32kb + 16j + 8g .. +7, i.e. P^T chunk kc = 2kb + j.
+  // partial row sum (fp32, unrounded), or, with e4m3 P, the operand and pk.
+  // Registers 8j .. 8j+7 of block kb hold keys 32kb + 16j + 8g .. +7, i.e.
+  // P^T chunk kc = 2kb + j.
   auto exp_tile = [&]() -> float {
     float lt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -369,11 +385,13 @@ __device__ __forceinline__ void fp8_tile(const AttnParams& p) {
               pf8[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf8[w], true);
             else
               pf8[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf8[w], false);
+            pk[16 * kb + r] = p0;
+            pk[16 * kb + r + 1] = p1;
           } else {
             pf[2 * kb + j][e2] = pack_bf16x2(p0, p1);
+            lt[e2] += p0;
+            lt[e2] += p1;
           }
-          lt[e2] += p0;
-          lt[e2] += p1;
         }
     return (lt[0] + lt[1]) + (lt[2] + lt[3]);
   };
@@ -391,11 +409,40 @@ __device__ __forceinline__ void fp8_tile(const AttnParams& p) {
         for (int r = 0; r < 16; ++r)
           s[kb][r] = (32 * kb + 16 * (r >> 3) + (r & 7) <= limit) ? s[kb][r] : -INFINITY;
     }
+    if constexpr (P8) {
+      // The reference moves on tile 0 and when a stored 2P would exceed 256,
+      // i.e. when c S > 8 for a score of the lane (tested before the exps).
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      if (v == 0 || __builtin_amdgcn_ballot_w64(!(mx * c <= 8.0f)) != 0) {
+        // Tile 0 holds key 0, visible to every row, so its maximum is finite.
+        mx = halfwave_max(mx) - lift;  // relative to m_ref
+        const float delta = (v == 0) ? mx : fmaxf(mx, 0.f);
+        if (v > 0) {
+          const float alpha = exp2_fast(-delta * c);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        }
+        m_ref += delta;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[r] = lift - m_ref;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+      }
+      exp_tile();
+      return;
+    }
     float l_tile = 0.f;
     bool rebase = (v == 0);
     if (!rebase) {
       l_tile = exp_tile();
-      rebase = __builtin_amdgcn_ballot_w64(!(l_tile <= (P8 ? kSumLimitP8 : kSumLimit))) != 0;
+      rebase = __builtin_amdgcn_ballot_w64(!(l_tile <= kSumLimit)) != 0;
     }
     if (rebase) {
       // Tile 0 holds key 0, visible to every row, so its maximum is finite.
