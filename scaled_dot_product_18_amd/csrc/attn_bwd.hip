@@ -67,6 +67,15 @@ __device__ __forceinline__ int dual_swz(int row) {
   return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
+// A pointer the whole wave holds, moved into scalar registers: a buffer
+// resource built from it then needs no per-lane loop around its loads.
+__device__ __forceinline__ void* uniform_ptr(const void* ptr) {
+  const unsigned long long a = (unsigned long long)ptr;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return (void*)(((unsigned long long)hi << 32) | lo);
+}
+
 // This wave's DMA loads of tile t of a row-major [rows, D] bf16 array, HBM ->
 // LDS (lane l of load i fills dst + 1024 i + 16 l). Rows at or past the end
 // fall outside the buffer's range and load as zeros.
@@ -74,7 +83,8 @@ template <int NLOAD>
 __device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int t, int total_bytes,
                                          const unsigned* off, unsigned char* dst) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + t * tile_bytes), (short)0, total_bytes - t * tile_bytes, kBufferConfig);
+      uniform_ptr(base + t * tile_bytes), (short)0, __builtin_amdgcn_readfirstlane(total_bytes - t * tile_bytes),
+      kBufferConfig);
 #pragma unroll
   for (int i = 0; i < NLOAD; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * i), 16, off[i], 0, 0, 0);
@@ -100,7 +110,7 @@ __device__ __forceinline__ int tr_offset(int lane, int db, int hi) {
 // HBM -> LDS, lane l filling dst + 4 l; rows past the end load as zeros.
 __device__ __forceinline__ void dma_stat(const float* base, int t, int total_bytes, int lane, unsigned char* dst) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(base + 64 * t), (short)0, total_bytes - 256 * t, kBufferConfig);
+      uniform_ptr(base + 64 * t), (short)0, __builtin_amdgcn_readfirstlane(total_bytes - 256 * t), kBufferConfig);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, 4 * lane, 0, 0, 0);
 }
 
@@ -248,43 +258,65 @@ void attn_bwd_dq_kernel(const BwdParams p) {
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
   const float c = p.qk_scale_log2;
 
+  // Query qi sees keys [0, vis_end): the causal bound and the sequence end.
+  const int vis_end = CAUSAL ? min(p.Sk, qi + 1 + p.causal_off) : p.Sk;
+  constexpr int LA = 4;  // MFMAs whose LDS operand reads are in flight ahead
+
+  // S^T and dP^T of key block kb (32 keys) of a tile: S and dP MFMAs
+  // alternate, each A operand read LA MFMAs ahead of the matrix core.
+  auto sdp = [&](const unsigned char* kl, const unsigned char* vl, int kb, f32x16& s, f32x16& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int st = 0; st < C::QS; ++st) {
+      const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[st]), s,
+                                                  0, 0, 0);
+      const u32x4 b = *(const u32x4*)(vl + kb * 32 * C::RB + v_rd[st]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, dof[st]),
+                                                   dp, 0, 0, 0);
+    }
+    constexpr int N = 2 * C::QS;
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + LA < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // dS^T of key block kb rounded to bf16: dsf[2kb + j], element e <-> key
+  // 32kb + 16j + 8(e/4) + 4g + e%4 of the tile. In blocks that reach past a
+  // lane's visible keys the masked entries are set to 0 (a select, so an
+  // overflowing exp of a masked score cannot leak).
+  auto dscore = [&](int kv0, int kb, const f32x16& s, const f32x16& dp, u32x4* dsf) {
+    const int kb0 = kv0 + 32 * kb;
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = exp2_fast(__builtin_fmaf(s[r], c, -lse2)) * (dp[r] - dlt);
+    const bool edge = (CAUSAL && kb0 + 31 > qw + p.causal_off) || kb0 + 32 > p.Sk;
+    if (edge) {
+      const int rel = vis_end - kb0 - 4 * g;  // register r (key kb0 + 8(r/4) + 4g + r%4) is visible iff below
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = (8 * (r >> 2) + (r & 3) < rel) ? ds[r] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) dsf[2 * kb + j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
+  };
+
   auto compute_tile = [&](int kt, const unsigned char* kl, const unsigned char* vl) {
     const int kv0 = kt * C::BT;
-    u32x4 dsf[4];  // dS^T operand: chunk kc, element e <-> key 16kc + 8(e/4) + 4g + e%4
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int st = 0; st < C::QS; ++st) {
-        const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[st]),
-                                                    s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int st = 0; st < C::QS; ++st) {
-        const u32x4 a = *(const u32x4*)(vl + kb * 32 * C::RB + v_rd[st]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                     __builtin_bit_cast(bf16x8, dof[st]), dp, 0, 0, 0);
-      }
-      // register r on half g: key kv0 + 32kb + 8(r/4) + 4g + r%4
-      const int kb0 = kv0 + 32 * kb;
-      const bool edge = (CAUSAL && kb0 + 31 > qw + p.causal_off) || kb0 + 32 > p.Sk;
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = exp2_fast(__builtin_fmaf(s[r], c, -lse2));
-        if (edge) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < p.Sk && (!CAUSAL || key <= qi + p.causal_off);
-          pr = ok ? pr : 0.f;
-        }
-        ds[r] = pr * (dp[r] - dlt);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) dsf[2 * kb + j][e2] = pack_bf16x2(ds[8 * j + 2 * e2], ds[8 * j + 2 * e2 + 1]);
-    }
+    u32x4 dsf[4];
+    f32x16 s, dp;
+    sdp(kl, vl, 0, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    dscore(kv0, 0, s, dp, dsf);
+    __builtin_amdgcn_sched_barrier(0);
+    sdp(kl, vl, 1, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    dscore(kv0, 1, s, dp, dsf);
     // dQ^T += K^T dS^T. Its own scheduling region: the two transposing reads
     // of each operand run LA MFMAs ahead of the matrix core.
     __builtin_amdgcn_sched_barrier(0);
@@ -294,7 +326,7 @@ void attn_bwd_dq_kernel(const BwdParams p) {
       for (int kc = 0; kc < 4; ++kc)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kl + 16 * kc * C::RB, kt_lo[db], kt_hi[db]),
                                                           __builtin_bit_cast(bf16x8, dsf[kc]), acc[db], 0, 0, 0);
-    constexpr int NUP = C::DB * 4, LA = 4;
+    constexpr int NUP = C::DB * 4;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
 #pragma unroll
     for (int i = 0; i < NUP; ++i) {
