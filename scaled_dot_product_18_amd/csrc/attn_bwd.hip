@@ -9,10 +9,11 @@
 //   P = exp(scale Q K^T - lse)         dV = P^T dO         dP = dO V^T
 //   dS = P * (dP - delta), delta_i = sum_c dO_ic O_ic    (= sum_j P_ij dP_ij)
 //   dQ = scale dS K                    dK = scale dS^T Q
-// Three kernels on one stream:
-//  * attn_bwd_delta_kernel: delta for every query row (caller's workspace);
+// Two kernels on one stream:
 //  * attn_bwd_dq_kernel: one workgroup per 128 queries of one (batch, query
-//    head), K/V tiles of 64 keys streamed HBM -> LDS as in the forward. The
+//    head); it first computes delta of its queries from their dO and O rows
+//    and stores it (with lse * log2(e)) in the caller's workspace for the
+//    second kernel. K/V tiles of 64 keys stream HBM -> LDS as in the forward. The
 //    products are transposed as in the forward kernels (lane = query column):
 //    S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16, the per-row
 //    lse and delta are lane scalars, and dS^T rounded to bf16 is directly the
@@ -153,32 +154,6 @@ __device__ __forceinline__ void store_tile(const f32x16* acc, float sc, unsigned
   }
 }
 
-// ---------------------------------------------------------------- delta
-// delta[row] = sum_c dO[row, c] * O[row, c] and lse2[row] = lse[row] * log2(e);
-// D/8 lanes per row, 8 elements each.
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void attn_bwd_delta_kernel(const BwdParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const size_t rows = (size_t)p.B * p.Hq * p.Sq;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int part = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = *(const u32x4*)((const unsigned char*)p.o + row * (2 * D) + 16 * part);
-    const u32x4 b = *(const u32x4*)((const unsigned char*)p.dout + row * (2 * D) + 16 * part);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc += bf16_lo(a[w]) * bf16_lo(b[w]) + bf16_hi(a[w]) * bf16_hi(b[w]);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && part == 0) {
-    p.delta[row] = acc * p.delta_mul;
-    p.lse2[row] = p.lse[row] * kLog2e;
-  }
-}
-
 // ---------------------------------------------------------------- dQ
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
@@ -237,9 +212,25 @@ void attn_bwd_dq_kernel(const BwdParams p) {
     dof[s] = ok ? *(const u32x4*)((const unsigned char*)p.dout + (qo_row0 + qi) * C::RB + 32 * s + 16 * g)
                 : u32x4{0, 0, 0, 0};
   }
-  // Padding rows (qi >= Sq) have Q = dO = 0, lse = delta = 0: every dS there is 0.
+  // delta = delta_mul * sum_c dO_c O_c of query qi: each half g of the wave
+  // holds half of the row's dims (the dO fragments above, the O fragments
+  // read here), and the halves meet across lanes l and l ^ 32. Half 0 also
+  // stores delta and lse2 = lse * log2(e) for the dK/dV kernel. Padding rows
+  // (qi >= Sq) have Q = dO = 0, lse = delta = 0: every dS there is 0.
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < C::QS; ++s) {
+    const u32x4 of = qi < p.Sq ? *(const u32x4*)((const unsigned char*)p.o + (qo_row0 + qi) * C::RB + 32 * s + 16 * g)
+                               : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dsum += bf16_lo(dof[s][w]) * bf16_lo(of[w]) + bf16_hi(dof[s][w]) * bf16_hi(of[w]);
+  }
+  const float dlt = halfwave_sum(dsum) * p.delta_mul;
   const float lse2 = qi < p.Sq ? p.lse[qo_row0 + qi] * kLog2e : 0.f;
-  const float dlt = qi < p.Sq ? p.delta[qo_row0 + qi] : 0.f;
+  if (g == 0 && qi < p.Sq) {
+    p.delta[qo_row0 + qi] = dlt;
+    p.lse2[qo_row0 + qi] = lse2;
+  }
 
   int k_rd[C::QS], v_rd[C::QS], kt_lo[C::DB], kt_hi[C::DB];
 #pragma unroll
@@ -450,6 +441,9 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   // Query tiles from the first one that sees a key of this workgroup (i >= k0 - off; all without the mask).
   const int t_first = CAUSAL ? max(0, k0 - off) / C::BT : 0;
   const int n_qt = (p.Sq + C::BT - 1) / C::BT;
+  // Tiles from t_nomask on lie wholly below the diagonal for every key of the
+  // workgroup (query 64 t sees key k0 + 127).
+  const int t_nomask = CAUSAL ? (k0 + 127 - off + C::BT - 1) / C::BT : 0;
 
   // The work of one 64-query tile t for this wave's 32 keys, in two 32-query
   // blocks qb (lane = key kj; register r on half g <-> query 32qb + 8(r/4) + 4g + r%4):
@@ -479,11 +473,26 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   auto a_operand = [&](int i, const unsigned char* ql, const unsigned char* ol, int qb) {
     return *(const u32x4*)((i >= C::QS ? ol : ql) + 32 * qb * C::RB + q_rd[i % C::QS]);
   };
+  // The mask enters S through the first MFMA's accumulator: s_init[qb] holds
+  // -inf where the query of a register cannot see this lane's key (so P =
+  // exp2(-inf) = 0 exactly) and 0 elsewhere; it is all zeros once the tiles
+  // are past the diagonal. Block 1 of the current tile and block 0 of the
+  // next are the ones a step starts.
+  f32x16 s_init[NB] = {f32x16{}, f32x16{}};
+  auto mask_init = [&](int t, int qb) {
+    const int vis = t * C::BT + off - kj + 4 * g;  // query 32qb+8m+4g+e sees kj iff vis + 32qb + 8m + e >= 0
+    f32x16 r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[4 * m + e] = (vis >= -(32 * qb + 8 * m + e)) ? 0.f : -__builtin_inff();
+    return r;
+  };
   auto a_mfma = [&](int i, int qb, u32x4 a) {
     const int st = i % C::QS;
     if (i < C::QS)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, kf[st]),
-                                                      st == 0 ? f32x16{} : s[qb], 0, 0, 0);
+                                                      st == 0 ? (CAUSAL ? s_init[qb] : f32x16{}) : s[qb], 0, 0, 0);
     else
       dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, vf[st]),
                                                        st == 0 ? f32x16{} : dp[qb], 0, 0, 0);
@@ -501,13 +510,11 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
       dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, dsf[qb][kc]), dk[db], 0, 0, 0);
   };
   // B group m of block qb with its statistics (lse2, delta of queries 32qb + 8m + 4g + 0..3).
-  auto b_group = [&](int t, int qb, int m, f32x4 l2, f32x4 dl) {
-    const int vis = t * C::BT + off - kj + 4 * g;  // query 32qb+8m+4g+e sees kj iff vis + 32qb + 8m + e >= 0
+  auto b_group = [&](int qb, int m, f32x4 l2, f32x4 dl) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * m + e;
-      float x = exp2_fast(__builtin_fmaf(s[qb][r], c, -l2[e]));
-      if (CAUSAL) x = (vis >= -(32 * qb + 8 * m + e)) ? x : 0.f;
+      const float x = exp2_fast(__builtin_fmaf(s[qb][r], c, -l2[e]));
       pr[qb][r] = x;
       ds[qb][r] = x * (dp[qb][r] - dl[e]);
     }
@@ -565,6 +572,10 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   auto step = [&](int t, unsigned char* qc, unsigned char* oc, float* sc, unsigned char* qn, unsigned char* on,
                   float* sn, unsigned char* qf_, unsigned char* of_, float* sf) {
     if (t + 2 < n_qt) load(t + 2, qf_, of_, sf);
+    if (CAUSAL && t <= t_nomask) {  // (at t_nomask both come out all zeros)
+      s_init[1] = mask_init(t, 1);
+      s_init[0] = mask_init(t + 1, 0);
+    }
 #pragma unroll
     for (int k = 0; k < NSUB; ++k) {
       const int part = k / SUBS, i0 = 4 * (k % SUBS);
@@ -595,7 +606,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
       }
       if (part < 2) {
 #pragma unroll
-        for (int h = 0; h < GPS; ++h) b_group(t, part, GPS * (k % SUBS) + h, l2[h], dl[h]);
+        for (int h = 0; h < GPS; ++h) b_group(part, GPS * (k % SUBS) + h, l2[h], dl[h]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -614,6 +625,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     if (t_first + 1 < n_qt) load(t_first + 1, q_lds1, o_lds1, st_lds1);
     __syncthreads();
     // A(t_first, 0), then the first step's operands
+    if (CAUSAL) s_init[0] = mask_init(t_first, 0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) a_mfma(i, 0, a_operand(i, q_lds0, o_lds0, 0));
     fetch(0, q_lds0, o_lds0, st_lds0, nullptr, nullptr);
@@ -684,12 +696,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_d(const BwdParams& bp, hipStream_t stream) {
   BwdParams arg = bp;
   void* args[] = {&arg};
-  const size_t rows = (size_t)bp.B * bp.Hq * bp.Sq;
-  constexpr int RPB = 256 / (D / 8);
-  hipError_t e = hipLaunchKernel((const void*)&attn_bwd_delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
-                                 dim3(256), args, 0, stream);
-  if (e != hipSuccess) return e;
-  e = hipLaunchKernel((const void*)&attn_bwd_dq_kernel<D, CAUSAL>,
+  hipError_t e = hipLaunchKernel((const void*)&attn_bwd_dq_kernel<D, CAUSAL>,
                       dim3((unsigned)bp.n_qtiles * (unsigned)bp.B * (unsigned)bp.Hq), dim3(256), args, 0, stream);
   if (e != hipSuccess) return e;
   e = hipLaunchKernel((const void*)&attn_bwd_dkdv_kernel<D, CAUSAL>,
