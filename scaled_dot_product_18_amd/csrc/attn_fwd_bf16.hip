@@ -100,15 +100,25 @@ __device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_byt
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+// SPLIT = 2: eight waves, the workgroup's keys in two halves. Waves 0-3 take
+// the first half of the key tiles and waves 4-7 the second, each with its
+// own K/V stages, so every SIMD runs two independent chains of tiles; the two
+// partial softmax states of a query row (reference maximum, normaliser,
+// unnormalised output) are merged through LDS at the end. For grids of at
+// most one workgroup per CU, where one wave per SIMD would leave the chain
+// of dependent steps exposed.
+template <int D, bool CAUSAL, bool READ_AHEAD, int SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256 * SPLIT, 256 * SPLIT), amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const AttnParams p) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem1[C::STAGE];
+  static_assert(SPLIT == 1 || (SPLIT == 2 && READ_AHEAD), "the key split runs with read-ahead");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem0[SPLIT * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem1[SPLIT * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and LDS bases
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and LDS bases
+  const int half = wave_id >> 2;                                 // key half (0 unless SPLIT = 2)
+  const int wave = wave_id & 3;                                  // 32-row block
   const int lane = tid & 63;
   const int i32 = lane & 31;
   const int g = lane >> 5;
@@ -150,6 +160,12 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
   const bool wave_active = qw < p.Sq;
   const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BN + 1) : n_tiles);
+  // This half's key tiles [t_lo, t_hi); n_steps tiles per half (the first half takes the odd one).
+  const int n_steps = SPLIT == 2 ? (n_tiles + 1) / 2 : n_tiles;
+  const int t_lo = half * n_steps;
+  const int t_hi = half == 0 ? n_steps : n_tiles;
+  unsigned char* const st0 = smem0 + half * C::STAGE;
+  unsigned char* const st1 = smem1 + half * C::STAGE;
 
   // ---- DMA assignment: wave w writes 1 KB blocks DMA*w .. DMA*w+DMA-1 of each tile
   // 16-byte slot s = 64*(DMA*w+t) + lane holds row s / CH, physical chunk s % CH.
@@ -187,7 +203,12 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // reference maximum, log2 units of the scaled score
+  // Reference maximum, log2 units of the scaled score. It starts at the most
+  // negative finite value, not -inf: under the key split the second half's
+  // first tiles can hide every key from a row, and exp2(c S - m) of those
+  // -inf scores must still come out 0 (with m = -inf it would be exp2(NaN)).
+  // The first tile with a visible key rescales by exp2(-FLT_MAX - m) = 0.
+  float m_run = -__FLT_MAX__;
   float l_run = 0.f;        // this lane's share of the normaliser
   const float c = p.qk_scale_log2;
 
@@ -196,16 +217,49 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
     const unsigned char* kl = stage;
     const unsigned char* vl = stage + C::TILE;
 
-    // S^T = K . Q^T
+    // S^T = K . Q^T. With READ_AHEAD every K operand is read first and the
+    // MFMAs of the KB independent blocks alternate; the V^T operands of the
+    // tile's P.V are read right behind them, so their latency hides under the
+    // softmax (32 more VGPRs: three resident waves per SIMD instead of four).
     f32x16 s[C::KB];
+    bf16x8 va[C::DB][C::KC];
+    auto v_operand = [&](int db, int kc) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc) * C::RB + v_rd[db]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc + 8) * C::RB + v_rd[db]));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    if constexpr (READ_AHEAD) {
+      u32x4 ka[C::KB][C::QS];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      s[kb] = f32x16{};
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int st = 0; st < C::QS; ++st) {
-        const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+        for (int st = 0; st < C::QS; ++st) ka[kb][st] = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::QS; ++st)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[kb][st]),
+                                                          __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) va[db][kc] = v_operand(db, kc);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::KB * C::QS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::KB * C::QS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::DB * C::KC, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < C::QS; ++st) {
+          const u32x4 a = *(const u32x4*)(kl + kb * 32 * C::RB + k_rd[st]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, qf[st]), s[kb], 0, 0, 0);
+        }
       }
     }
 
@@ -258,15 +312,11 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
 
     // O^T += V^T . P^T
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc) * C::RB + v_rd[db]));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vl + (16 * kc + 8) * C::RB + v_rd[db]));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < C::DB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(READ_AHEAD ? va[db][kc] : v_operand(db, kc),
+                                                          __builtin_bit_cast(bf16x8, pf[kc]), acc[db], 0, 0, 0);
   };
 
   // ---- main loop: DMA of tile kt+1 overlaps compute of tile kt --------------
@@ -274,38 +324,70 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   // key's row, so rows at or past Sk load as zeros.
   const int k_tile = C::BN * p.k_ss, v_tile = C::BN * p.v_ss;
   const int k_limit = (p.Sk - 1) * p.k_ss + C::RB, v_limit = (p.Sk - 1) * p.v_ss + C::RB;
-  if (n_tiles > 0) {
-    dma_tile<C::DMA>(kbase, k_tile, 0, k_limit, kdma_off, smem0 + 1024 * C::DMA * wave);
-    dma_tile<C::DMA>(vbase, v_tile, 0, v_limit, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
+  if (t_lo < t_hi) {
+    dma_tile<C::DMA>(kbase, k_tile, t_lo, k_limit, kdma_off, st0 + 1024 * C::DMA * wave);
+    dma_tile<C::DMA>(vbase, v_tile, t_lo, v_limit, vdma_off, st0 + C::TILE + 1024 * C::DMA * wave);
   }
   __syncthreads();
-  for (int kt = 0; kt < n_tiles; kt += 2) {
-    if (kt + 1 < n_tiles) {
-      dma_tile<C::DMA>(kbase, k_tile, kt + 1, k_limit, kdma_off, smem1 + 1024 * C::DMA * wave);
-      dma_tile<C::DMA>(vbase, v_tile, kt + 1, v_limit, vdma_off, smem1 + C::TILE + 1024 * C::DMA * wave);
+  for (int i = 0; i < n_steps; i += 2) {
+    const int kt = t_lo + i;
+    if (kt + 1 < t_hi) {
+      dma_tile<C::DMA>(kbase, k_tile, kt + 1, k_limit, kdma_off, st1 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, v_tile, kt + 1, v_limit, vdma_off, st1 + C::TILE + 1024 * C::DMA * wave);
     }
-    if (kt < wave_tiles) compute_tile(kt, smem0);
+    if (kt < t_hi && kt < wave_tiles) compute_tile(kt, st0);
     __syncthreads();
-    if (kt + 1 >= n_tiles) break;
-    if (kt + 2 < n_tiles) {
-      dma_tile<C::DMA>(kbase, k_tile, kt + 2, k_limit, kdma_off, smem0 + 1024 * C::DMA * wave);
-      dma_tile<C::DMA>(vbase, v_tile, kt + 2, v_limit, vdma_off, smem0 + C::TILE + 1024 * C::DMA * wave);
+    if (i + 1 >= n_steps) break;
+    if (kt + 2 < t_hi) {
+      dma_tile<C::DMA>(kbase, k_tile, kt + 2, k_limit, kdma_off, st0 + 1024 * C::DMA * wave);
+      dma_tile<C::DMA>(vbase, v_tile, kt + 2, v_limit, vdma_off, st0 + C::TILE + 1024 * C::DMA * wave);
     }
-    if (kt + 1 < wave_tiles) compute_tile(kt + 1, smem1);
+    if (kt + 1 < t_hi && kt + 1 < wave_tiles) compute_tile(kt + 1, st1);
     __syncthreads();
+  }
+
+  // ---- merge of the two key halves (SPLIT = 2) -------------------------------
+  // The second half's waves leave acc, m_run and l_run in LDS (register-major,
+  // 64 lanes contiguous: acc in smem0, m and l at the end of smem1); the first
+  // half's wave of the same rows rescales both to the larger reference and
+  // adds. A row always has key 0, so the first half's reference is a real
+  // score maximum; an empty second half (m = -FLT_MAX) gets the factor 0.
+  if constexpr (SPLIT == 2) {
+    float* const m_acc = (float*)smem0 + wave * (C::DB * 16 * 64);
+    float* const m_ml = (float*)(smem1 + 2 * C::STAGE) - 8 * 64 + wave * (2 * 64);
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m_acc[(db * 16 + r) * 64 + lane] = acc[db][r];
+      m_ml[lane] = m_run;
+      m_ml[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (half == 1 || !wave_active) return;
+    const float m_b = m_ml[lane], l_b = m_ml[64 + lane];
+    const float m_new = fmaxf(m_run, m_b);
+    const float fa = exp2_fast(m_run - m_new), fb = exp2_fast(m_b - m_new);
+    m_run = m_new;
+    l_run = l_run * fa + l_b * fb;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * fa + m_acc[(db * 16 + r) * 64 + lane] * fb;
   }
 
   // ---- epilogue -------------------------------------------------------------
   // O = acc / l rounded to bf16. A lane holds 4-dim pieces of one query row,
   // so the wave writes its 32-row tile to LDS (stage buffer 0 is idle after
-  // the last barrier; wave w takes rows [32w, 32w+32) of it) and reads it back
+  // the last barrier, buffer 1 after a merge; wave w takes rows [32w, 32w+32)
+  // of it) and reads it back
   // as whole rows, so that each global store covers 1 KB of contiguous rows.
   // 16-byte chunks are XOR-swizzled by row. The stores carry the non-temporal
   // hint: nothing in the kernel reads O back.
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
   const float inv = 1.0f / l_tot;
-  unsigned char* stage = smem0 + wave * (32 * C::RB);
+  unsigned char* stage = (SPLIT == 2 ? smem1 : smem0) + wave * (32 * C::RB);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -327,12 +409,27 @@ void attn_fwd_bf16_kernel(const AttnParams p) {
   if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
+// Grids that fit in one round at three workgroups per CU (768) are bound by
+// each wave's chain of dependent steps: there the operand reads run ahead.
+// Larger grids keep four resident waves per SIMD.
+constexpr unsigned kReadAheadMaxGrid = 768;
+
+// Grids of at most one workgroup per CU split each workgroup's keys over
+// eight waves, when there are enough key tiles (six) to pay for the merge.
+constexpr unsigned kSplitMaxGrid = 256;
+constexpr int kSplitMinKeys = 384;
+
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
   AttnParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<D, CAUSAL>, dim3(grid), dim3(256), args, 0, stream);
+  if (grid <= kSplitMaxGrid && p.Sk >= kSplitMinKeys)
+    return hipLaunchKernel((const void*)&attn_fwd_bf16_kernel<D, CAUSAL, true, 2>, dim3(grid), dim3(512), args, 0,
+                           stream);
+  const void* fn = grid <= kReadAheadMaxGrid ? (const void*)&attn_fwd_bf16_kernel<D, CAUSAL, true, 1>
+                                             : (const void*)&attn_fwd_bf16_kernel<D, CAUSAL, false, 1>;
+  return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, stream);
 }
 
 int bf16_block_m(int d) { return d == 128 ? bf16_pp_block_m() : Bf16Cfg<64>::BM; }

@@ -56,6 +56,27 @@ def test_bf16_tails(gpu, S, d, causal, heads):
     _run_full(w)
 
 
+# bf16 at d = 32 and 64: grids of at most 256 workgroups with at least 384
+# keys split each workgroup's keys over eight waves (two halves of the key
+# tiles, merged at the end); other grids up to 768 workgroups read operands
+# ahead with four waves; larger grids take the plain four-wave form. Odd and
+# even tile counts, the 383/384-key and 256/264-workgroup boundaries, causal
+# rows whose second half sees no key (Sq < Sk), ragged tails, GQA and MQA.
+SMALL_D_FORMS = [
+    (1, 4, 2, 384, 384, 64, False), (1, 4, 2, 383, 383, 64, True), (1, 4, 4, 449, 449, 64, True),
+    (2, 4, 1, 700, 700, 64, False), (1, 8, 2, 130, 1000, 64, True), (2, 4, 2, 5, 1000, 64, True),
+    (1, 8, 8, 1024, 1024, 32, True), (1, 4, 2, 77, 640, 32, False), (1, 32, 8, 1024, 1024, 64, True),
+    (1, 33, 11, 1024, 1024, 64, False), (4, 12, 4, 520, 520, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d,causal", SMALL_D_FORMS)
+def test_bf16_small_head_dim_forms(gpu, B, Hq, Hkv, Sq, Sk, d, causal):
+    stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, d, "bf16", causal, seed=31000 + Sq + Sk + Hq,
+                                         want_lse=True))
+    log(f"  {stats}")
+
+
 @pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (32, 64, 128),
                                                                     (False, True), [(4, 4), (4, 2), (4, 1)])))
 def test_f32_tails(gpu, S, d, causal, heads):
