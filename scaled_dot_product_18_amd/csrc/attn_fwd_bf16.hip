@@ -10,8 +10,11 @@
 // its section 7 and the shared KV heads of its section 9.
 //
 // Layout of the work on CDNA4:
-//  * this four-wave kernel serves head dimensions 32 and 64 (the eight-wave
-//    ping-pong kernel in attn_fwd_bf16_pp.hip serves 128);
+//  * this kernel serves head dimensions 32 and 64 (the eight-wave ping-pong
+//    kernel in attn_fwd_bf16_pp.hip serves 128), in three forms picked by
+//    the grid: four waves with four resident per SIMD (large grids), four
+//    waves with the operand reads run ahead (up to 768 workgroups), and eight
+//    waves splitting the keys in two halves (up to 256 workgroups);
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //    wave w owns rows [32w, 32w+32) and keeps their Q fragment in VGPRs;
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16,
