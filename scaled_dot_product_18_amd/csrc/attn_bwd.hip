@@ -626,8 +626,15 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     __syncthreads();
     // A(t_first, 0), then the first step's operands
     if (CAUSAL) s_init[0] = mask_init(t_first, 0);
+    // (the operands in batches of eight, read before their MFMAs)
 #pragma unroll
-    for (int i = 0; i < NP; ++i) a_mfma(i, 0, a_operand(i, q_lds0, o_lds0, 0));
+    for (int i0 = 0; i0 < NP; i0 += 8) {
+      u32x4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = a_operand(i0 + u, q_lds0, o_lds0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a_mfma(i0 + u, 0, a[u]);
+    }
     fetch(0, q_lds0, o_lds0, st_lds0, nullptr, nullptr);
     for (int t = t_first;;) {
       step(t, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1, q_lds2, o_lds2, st_lds2);
