@@ -11,10 +11,12 @@
 //
 // Layout of the work on CDNA4:
 //  * this kernel serves head dimensions 32 and 64 (the eight-wave ping-pong
-//    kernel in attn_fwd_bf16_pp.hip serves 128), in three forms picked by
-//    the grid: four waves with four resident per SIMD (large grids), four
-//    waves with the operand reads run ahead (up to 768 workgroups), and eight
-//    waves splitting the keys in two halves (up to 256 workgroups);
+//    kernel in attn_fwd_bf16_pp.hip serves 128, and the one in
+//    attn_fwd_bf16_pp64.hip d = 64 grids of up to 768 workgroups over at
+//    least 1024 keys), in three forms picked by the grid: four waves with
+//    four resident per SIMD (large grids), four waves with the operand reads
+//    run ahead (up to 768 workgroups), and eight waves splitting the keys in
+//    two halves (up to 256 workgroups);
 //  * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //    wave w owns rows [32w, 32w+32) and keeps their Q fragment in VGPRs;
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16,
@@ -422,9 +424,18 @@ constexpr unsigned kReadAheadMaxGrid = 768;
 constexpr unsigned kSplitMaxGrid = 256;
 constexpr int kSplitMinKeys = 384;
 
+// d = 64 grids of up to 768 workgroups over at least 1024 keys run the
+// ping-pong kernel (16 or more key tiles per row; on shorter rows, and on
+// larger grids, where four waves per SIMD overlap without barriers, it is
+// no faster).
+constexpr unsigned kPingPongMaxGrid = 768;
+constexpr int kPingPongMinKeys = 1024;
+
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
+  if (D == 64 && grid <= kPingPongMaxGrid && p.Sk >= kPingPongMinKeys)
+    return launch_attn_bf16_pp64(p, CAUSAL, stream);
   AttnParams arg = p;
   void* args[] = {&arg};
   if (grid <= kSplitMaxGrid && p.Sk >= kSplitMinKeys)

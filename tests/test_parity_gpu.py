@@ -77,6 +77,27 @@ def test_bf16_small_head_dim_forms(gpu, B, Hq, Hkv, Sq, Sk, d, causal):
     log(f"  {stats}")
 
 
+# bf16 at d = 64, grids of at most 768 workgroups over at least 1024 keys: the
+# eight-wave ping-pong kernel, each workgroup's key tiles in two halves run in
+# anti-phase and merged at the end. Odd and even tile counts (17 tiles of 1030
+# keys, 18 of 1100), ragged unmasked tails, a causal offset that is not a
+# multiple of 32 (rows of one wave that do and do not see the second half's
+# first tile), the second half hidden from whole waves (first q-tile; Sq < Sk
+# with waves past Sq), GQA and MQA, and the 768-workgroup boundary.
+PP64_FORMS = [
+    (1, 4, 2, 1000, 1040, True), (1, 4, 4, 1030, 1030, True), (2, 4, 2, 300, 1100, False),
+    (1, 8, 2, 130, 1500, True), (1, 8, 1, 1024, 1024, True), (2, 3, 1, 2000, 2000, False),
+    (2, 48, 12, 1024, 1024, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", PP64_FORMS)
+def test_bf16_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
+    stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, 64, "bf16", causal, seed=32000 + Sq + Sk + Hq,
+                                         want_lse=True))
+    log(f"  {stats}")
+
+
 @pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (32, 64, 128),
                                                                     (False, True), [(4, 4), (4, 2), (4, 1)])))
 def test_f32_tails(gpu, S, d, causal, heads):

@@ -60,6 +60,23 @@ def test_codelab_layout_key_split(gpu, d, causal):
     assert torch.equal(o_bhsd, o_ref) and torch.equal(lse, lse_ref)
 
 
+@pytest.mark.parametrize("causal", (False, True))
+def test_codelab_layout_ping_pong(gpu, causal):
+    """bf16 at d = 64 with 1100 keys on a small grid: the eight-wave ping-pong kernel reads and
+    writes (B, T, N, H) in place and equals its dense result bit for bit."""
+    w = sdpa_inputs.custom(2, 4, 2, 1100, 1100, 64, "bf16", causal, seed=15600, want_lse=True)
+    log(f"[strided] {w.name} bshd ping-pong")
+    inp = sdpa_inputs.make_inputs(w)
+    dev = to_device(inp)
+    o_ref, lse_ref = run_gpu(w, dev)
+    qs, ks, vs = (dev[n].transpose(1, 2).contiguous() for n in ("q", "k", "v"))
+    o, lse = _call(w, dev, qs, ks, vs, layout="bshd")
+    torch.cuda.synchronize()
+    o_bhsd = o.transpose(1, 2)
+    check_full(w, inp, o_bhsd, lse)
+    assert torch.equal(o_bhsd, o_ref) and torch.equal(lse, lse_ref)
+
+
 @pytest.mark.parametrize("dtype,d", list(itertools.product(("f32", "bf16", "fp8"), (64, 128))))
 def test_padded_rows_and_mixed_layouts(gpu, dtype, d):
     """q is every other row block of a wider tensor (position stride 2d), k and v are
