@@ -431,6 +431,10 @@ constexpr int kSplitMinKeys = 384;
 constexpr unsigned kPingPongMaxGrid = 768;
 constexpr int kPingPongMinKeys = 1024;
 
+// attn_fwd_bf16_pp64.hip: bf16, d = 64, eight waves in ping-pong over the two
+// halves of each workgroup's keys (n_qtiles counted in 128-row tiles, as here).
+hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream);
+
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;

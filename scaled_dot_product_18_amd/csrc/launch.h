@@ -21,10 +21,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t
 // bf16, d = 128: eight waves in matrix-core / vector-unit ping-pong.
 hipError_t launch_attn_bf16_pp(const AttnParams& p, bool causal, hipStream_t stream);
 
-// bf16, d = 64: eight waves in ping-pong over the two halves of each
-// workgroup's keys (n_qtiles counted in 128-row tiles, as for launch_attn_bf16).
-hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream);
-
 // fp8-e4m3fn inputs, bf16 output; d in {64, 128} (d = 128 runs the eight-wave
 // ping-pong kernel).
 hipError_t launch_attn_fp8(const AttnParams& p, int d, bool causal, hipStream_t stream);
