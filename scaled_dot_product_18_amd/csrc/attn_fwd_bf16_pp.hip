@@ -269,12 +269,10 @@ void attn_fwd_bf16_pp_kernel(const AttnParams p) {
                                                         0, 0, 0);
       }
   };
-  // M phase m (0 <= m <= T), one straight-line shape for every m: for m = 0
-  // the P operand is still zero and the V slot was zeroed in the prologue,
-  // so the product adds nothing; for m = T the K slot holds a stale tile and
-  // the scores it yields are never read. The LDS operand reads run LA MFMAs
-  // ahead of the matrix core (two transposing reads per P.V MFMA, one read
-  // per Q.K^T MFMA).
+  // M phase m (1 <= m <= T; M(0) is m_first below), one straight-line shape
+  // for every m: for m = T the K slot holds a stale tile and the scores it
+  // yields are never read. The LDS operand reads run LA MFMAs ahead of the
+  // matrix core (two transposing reads per P.V MFMA, one read per Q.K^T MFMA).
   auto m_phase = [&](int m, const unsigned char* kl, const unsigned char* vl) {
     if (m > T) return;
     pv_part(vl);
