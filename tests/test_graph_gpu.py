@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("bf16", 128, True, (2, 8, 2, 300, 300)),
     ("bf16", 64, False, (2, 4, 4, 196, 196)),
+    ("bf16", 64, True, (1, 4, 2, 1100, 1100)),  # the d = 64 ping-pong kernel (1024+ keys)
     ("fp8", 128, True, (1, 4, 1, 257, 257)),
     ("f32", 64, True, (1, 2, 2, 129, 129)),
 ]

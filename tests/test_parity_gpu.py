@@ -98,6 +98,11 @@ def test_bf16_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
     log(f"  {stats}")
 
 
+def test_bf16_d64_ping_pong_without_lse(gpu):
+    """The same kernel with no lse output requested (the store is skipped)."""
+    _run_full(sdpa_inputs.custom(2, 4, 2, 700, 1300, 64, "bf16", True, seed=32500), want_lse=False)
+
+
 @pytest.mark.parametrize("S,d,causal,heads", list(itertools.product([1, 17, 64, 65, 129, 257], (32, 64, 128),
                                                                     (False, True), [(4, 4), (4, 2), (4, 1)])))
 def test_f32_tails(gpu, S, d, causal, heads):
