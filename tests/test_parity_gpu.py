@@ -328,6 +328,20 @@ def test_full_size_workload_sampled(gpu, name):
     log(f"  {stats}")
 
 
+@pytest.mark.parametrize("name", ["kv_heads_2_bf16_b2_t4096", "causal_bf16_b4_t2048", "seq_len_bf16_b4_t1024"])
+def test_codelab_sweep_shapes_sampled(gpu, name):
+    """The codelab's own d = 64 sweep shapes that run the ping-pong kernel (1024+ keys), at
+    their full size, on sampled rows: the first rows, tile edges, the last rows and random rows."""
+    import bench
+    w = {x.name: x for _, x in bench.sweep_shapes()}[name]
+    log(f"[parity-sweep] {w.name}")
+    inp = sdpa_inputs.make_inputs(w)
+    o, lse = run_gpu(w, to_device(inp), want_lse=True)
+    torch.cuda.synchronize()
+    stats = check_sampled(w, inp, o, lse, n_random=48, first=32)
+    log(f"  {stats}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_sampled_causal_queries_against_longer_keys(gpu, dtype):
     """Causal, Sq < Sk at a size checked on sampled rows: query i sees keys j <= i + (Sk - Sq)."""
