@@ -12,7 +12,7 @@
 // Layout of the work on CDNA4:
 //  * this kernel serves head dimensions 32 and 64 (the eight-wave ping-pong
 //    kernel in attn_fwd_bf16_pp.hip serves 128, and the one in
-//    attn_fwd_bf16_pp64.hip d = 64 grids of up to 768 workgroups over at
+//    attn_fwd_pp64.hip d = 64 grids of up to 768 workgroups over at
 //    least 1024 keys), in three forms picked by the grid: four waves with
 //    four resident per SIMD (large grids), four waves with the operand reads
 //    run ahead (up to 768 workgroups), and eight waves splitting the keys in
@@ -431,7 +431,7 @@ constexpr int kSplitMinKeys = 384;
 constexpr unsigned kPingPongMaxGrid = 768;
 constexpr int kPingPongMinKeys = 1024;
 
-// attn_fwd_bf16_pp64.hip: bf16, d = 64, eight waves in ping-pong over the two
+// attn_fwd_pp64.hip: bf16, d = 64, eight waves in ping-pong over the two
 // halves of each workgroup's keys (n_qtiles counted in 128-row tiles, as here).
 hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream);
 

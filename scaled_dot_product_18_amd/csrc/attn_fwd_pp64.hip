@@ -1,6 +1,6 @@
-// Fused scaled dot-product attention forward for gfx950, bf16, head dim 64:
-// eight waves in matrix-core / vector-unit ping-pong over the two halves of a
-// workgroup's keys.
+// Fused scaled dot-product attention forward for gfx950 at head dim 64, on bf16
+// or fp8-e4m3fn inputs (bf16 output): eight waves in matrix-core / vector-unit
+// ping-pong over the two halves of a workgroup's keys.
 //
 // The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
 // and FlashAttention", section 3): K and V stream through on-chip tiles, the
@@ -25,14 +25,25 @@
 // LDS and group 0 merges the two halves, as two blocks of the same softmax.
 //
 // K/V: each group streams its own tiles through its own two K and two V slots
-// (8 KB each, 64 KB for the workgroup). Both groups load their K(n+1) and V(n)
-// HBM -> LDS (buffer_load ... lds, 2 KB per wave) in global phase 2n, group 0
-// after the MFMAs of its M(n), group 1 at the start of its V(n-1), and wait
-// for them at the barrier that ends phase 2n+1. Tile
-// layouts and swizzles are those of the four-wave d = 64 kernel: S^T and O^T
-// are computed transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one
+// (8 KB each, 64 KB for the workgroup with bf16 inputs). Both groups load their
+// K(n+1) and V(n) HBM -> LDS (buffer_load ... lds, 2 KB per wave) in global
+// phase 2n, group 0 after the MFMAs of its M(n), group 1 at the start of its
+// V(n-1), and wait for them at the barrier that ends phase 2n+1. Tile layouts
+// and swizzles are those of the four-wave d = 64 kernel: S^T and O^T are
+// computed transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one
 // query column, the bf16-rounded score accumulator is the P^T operand, and V^T
 // comes from the row-major V tile through ds_read_b64_tr_b16.
+//
+// e4m3 inputs: S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// E8M0 scales, one MFMA per 32-key block (its K depth of 64 is the whole head
+// dim), into the same accumulator layout, so the softmax, P and the P.V MFMAs
+// are those of the bf16 form. K tiles (4 KB of e4m3) go HBM -> LDS by DMA. V
+// tiles go HBM -> registers (16 codes per lane) and are widened exactly to
+// bf16 into the bf16 V layout at the end of an M phase, the short one at
+// d = 64: group 0 loads V(n+1) after its M(n) and stores it after its M(n+1),
+// group 1 loads V(n) at the start of its V(n-1) and stores it after its M(n).
+// The descales of Q and K are folded into the exponent's multiplier and that
+// of V into the final 1/l.
 //
 // Softmax reference: as in the d = 128 ping-pong kernel, the first Q.K^T MFMA
 // of a tile starts from -m_ref, the reference is set from the first tile with
@@ -53,10 +64,13 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int D = 64;
 constexpr int BM = 128;               // query rows per workgroup: four 32-row blocks, one per SIMD
 constexpr int BN = 64;                // keys per tile
-constexpr int RB = D * 2;             // bytes per K/V row
+constexpr int RB = D * 2;             // bytes per bf16 K/V row in LDS
 constexpr int CH = RB / 16;           // 16-byte chunks per row
 constexpr int TILE = BN * RB;         // 8 KB
 constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide loads per tensor per wave (a group's 4 waves fill a tile)
+constexpr int RB8 = D;                // bytes per e4m3 K/V row
+constexpr int TILE8 = BN * RB8;       // 4 KB
+constexpr int kE8M0One = 127;         // E8M0 block scale 2^0 of the fp8 MFMA
 constexpr int KB = BN / 32;           // 32-key blocks of a score tile
 constexpr int KC = BN / 16;           // 16-key chunks (K depth of P.V)
 constexpr int DB = D / 32;            // 32-wide output blocks
@@ -74,16 +88,20 @@ constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource (g
 // 4 rows of a transposing read hit disjoint 32-byte pairs).
 __device__ __forceinline__ int k_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int v_swizzle(int row) { return (0x6420 >> (4 * (row & 3))) & 15; }
+// e4m3 K rows (64 bytes, 4 chunks): 16 consecutive rows at one logical chunk hit
+// 4 rows per 256 bytes of banks, which the XOR with bits 2-3 of the row spreads.
+__device__ __forceinline__ int k8_swizzle(int row) { return (row >> 2) & 3; }
 
 // This wave's share of one K or V tile, HBM -> LDS: lane l of load t fills the
 // 16 bytes at dst + 1024 t + 16 l. The buffer starts at the tile's first row
 // and ends with the sequence's last, so rows at or past Sk load as zeros.
+template <int NL>
 __device__ __forceinline__ void dma_tile(const unsigned char* base, int tile_bytes, int kt, int limit,
                                          const unsigned* off, unsigned char* dst) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(base + kt * tile_bytes), (short)0, limit - kt * tile_bytes, kBufferConfig);
 #pragma unroll
-  for (int t = 0; t < DMA; ++t)
+  for (int t = 0; t < NL; ++t)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * t), 16, off[t], 0, 0, 0);
 }
 
@@ -101,16 +119,20 @@ __device__ __forceinline__ void barrier_after() {
   asm volatile("" ::: "memory");
 }
 
-template <bool CAUSAL>
+template <bool FP8, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
+void attn_fwd_pp64_kernel(const AttnParams p) {
+  constexpr int KTILE = FP8 ? TILE8 : TILE;     // K slot bytes
+  constexpr int KDMA = KTILE / 1024 / 4;        // 1 KB K loads per wave
+  constexpr int KCH = (FP8 ? RB8 : RB) / 16;    // 16-byte chunks per K row
+  constexpr int IRB = FP8 ? RB8 : RB;           // bytes per input K/V row
   // Slots of group 0 (first key half) and group 1, each a fixed LDS object.
-  __shared__ __attribute__((aligned(1024))) unsigned char k0_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k0_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k0_lds0[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k0_lds1[KTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v0_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v0_lds1[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k1_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char k1_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1_lds0[KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1_lds1[KTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v1_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char v1_lds1[TILE];
 
@@ -154,7 +176,7 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
   const unsigned char* kbase = head_ptr(p.k, p.k_sb, p.k_sh, b, hk);
   const unsigned char* vbase = head_ptr(p.v, p.v_sb, p.v_sh, b, hk);
   const int k_tile = BN * p.k_ss, v_tile = BN * p.v_ss;
-  const int k_limit = (p.Sk - 1) * p.k_ss + RB, v_limit = (p.Sk - 1) * p.v_ss + RB;
+  const int k_limit = (p.Sk - 1) * p.k_ss + IRB, v_limit = (p.Sk - 1) * p.v_ss + IRB;
 
   // Key tiles of the workgroup: [0, h) for group 0, [h, n_tiles) for group 1.
   // T counts this wave's tiles of its half (those up to the last one holding
@@ -171,29 +193,50 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
   const int full_tiles = CAUSAL ? min(p.Sk / BN, (qw + 1 + p.causal_off) / BN) : p.Sk / BN;
 
   // ---- DMA: wave si of a group writes 1 KB blocks DMA*si .. DMA*si+DMA-1 of each tile
-  unsigned kdma_off[DMA], vdma_off[DMA];
-  const int dma_pchunk = lane % CH;
+  unsigned kdma_off[KDMA], vdma_off[DMA];
+#pragma unroll
+  for (int t = 0; t < KDMA; ++t) {
+    const int row = (64 * (KDMA * si + t) + lane) / KCH;
+    kdma_off[t] = row * p.k_ss + 16 * ((lane % KCH) ^ (FP8 ? k8_swizzle(row) : k_swizzle(row)));
+  }
 #pragma unroll
   for (int t = 0; t < DMA; ++t) {
     const int row = (64 * (DMA * si + t) + lane) / CH;
-    kdma_off[t] = row * p.k_ss + 16 * (dma_pchunk ^ k_swizzle(row));
-    vdma_off[t] = row * p.v_ss + 16 * (dma_pchunk ^ v_swizzle(row));
+    vdma_off[t] = row * p.v_ss + 16 * ((lane % CH) ^ v_swizzle(row));
   }
-  const int dma_dst = 1024 * DMA * si;
+  const int kdma_dst = 1024 * KDMA * si, dma_dst = 1024 * DMA * si;
+  // e4m3 V: lane l of wave si loads 16 codes, dims [16 (l%4), +16) of row
+  // 16 si + l/4, and stores them widened (exactly) to bf16 as two 16-byte
+  // chunks of the row-major bf16 V tile.
+  const int v8_row = 16 * si + (lane >> 2), v8_piece = lane & 3;
+  const unsigned v8_ld = v8_row * p.v_ss + 16 * v8_piece;
+  const int v8_st0 = v8_row * RB + 16 * ((2 * v8_piece) ^ v_swizzle(v8_row));
+  const int v8_st1 = v8_row * RB + 16 * ((2 * v8_piece + 1) ^ v_swizzle(v8_row));
+  u32x4 v8reg = u32x4{0, 0, 0, 0};
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8) of row qi
   const float c = p.qk_scale_log2;
   u32x4 qf[QS];
+  i32x8 qf8 = i32x8{};  // e4m3: dims [32g, +32) of row qi, the B operand of the fp8 score MFMA
+  if constexpr (FP8) {
+    if (qi < p.Sq) {
+      const u32x4 a0 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * g);
+      const u32x4 a1 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * g + 16);
+      qf8 = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    }
+  } else {
 #pragma unroll
-  for (int s = 0; s < QS; ++s)
-    qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < QS; ++s)
+      qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
+  }
 
   // ---- LDS operand offsets: K row 32kb + i32 at logical chunk 2s + g; V^T
   // through the transposing read (lane J of a 16-lane group reads 4 dims of
   // key row 4g + J/4).
   int k_rd[QS];
 #pragma unroll
-  for (int s = 0; s < QS; ++s) k_rd[s] = i32 * RB + 16 * ((2 * s + g) ^ k_swizzle(i32));
+  for (int s = 0; s < QS; ++s)
+    k_rd[s] = FP8 ? i32 * RB8 + 16 * ((2 * g + (s & 1)) ^ k8_swizzle(i32)) : i32 * RB + 16 * ((2 * s + g) ^ k_swizzle(i32));
   const int J = lane & 15;
   int v_rd[DB];
 #pragma unroll
@@ -234,15 +277,27 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
       }
   };
   auto qk_part = [&](const unsigned char* kl) {
-#pragma unroll
-    for (int st = 0; st < QS; ++st)
+    if constexpr (FP8) {
+      // one fp8 MFMA (K depth 64 = d) per 32-key block; lane (i32, g) supplies
+      // key row i32's dims [32g, +32)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 a = *(const u32x4*)(kl + kb * 32 * RB + k_rd[st]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, qf[st]), st == 0 ? negm : s[kb],
-                                                        0, 0, 0);
+        const u32x4 a0 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[0]);
+        const u32x4 a1 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[1]);
+        const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8, negm, 0, 0, 0, kE8M0One, 0, kE8M0One);
       }
+    } else {
+#pragma unroll
+      for (int st = 0; st < QS; ++st)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 a = *(const u32x4*)(kl + kb * 32 * RB + k_rd[st]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, qf[st]), st == 0 ? negm : s[kb],
+                                                          0, 0, 0);
+        }
+    }
   };
   // M phase m (1 <= m <= T): for m = T the K slot holds a stale tile whose
   // scores are never read. The LDS operand reads run LA MFMAs ahead of the
@@ -251,7 +306,8 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
     if (m > T) return;
     pv_part(vl);
     qk_part(kl);
-    constexpr int NPV = KC * DB, NMF = KC * DB + KB * QS;
+    constexpr int NQK = FP8 ? KB : KB * QS, RQK = FP8 ? 2 : 1;  // score MFMAs, reads per score MFMA
+    constexpr int NPV = KC * DB, NMF = KC * DB + NQK;
     static_assert(LA <= NPV, "the prologue reads belong to P.V MFMAs");
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
 #pragma unroll
@@ -261,19 +317,21 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
       if (j < NPV)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       else if (j < NMF)
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RQK, 0);
     }
   };
   // M(0): no probabilities yet, so only S(0).
   auto m_first = [&](const unsigned char* kl) {
     if (T == 0) return;
     qk_part(kl);
-    constexpr int NQK = KB * QS;
-    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+    if constexpr (!FP8) {
+      constexpr int NQK = KB * QS;
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + LA < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < NQK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + LA < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
   // p = exp2(c S) for the whole tile: the P^T operand of the next M phase
@@ -342,10 +400,39 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
     }
     l_run += l_tile;
   };
-  // Loads of the group's K(n+1) and V(n) (tile indices within its half).
+  // e4m3 V tile n of the half into registers, and from there into a slot.
+  auto load_v8 = [&](int n) {
+    if (n >= n_mine) return;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (lo + n) * v_tile), (short)0, v_limit - (lo + n) * v_tile, kBufferConfig);
+    v8reg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, v8_ld, 0, 0));
+  };
+  auto store_v8 = [&](int n, unsigned char* dst) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (n >= n_mine) return;
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[j], 1.0f, false));
+      w[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[j], 1.0f, true));
+    }
+    *(u32x4*)(dst + v8_st0) = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4*)(dst + v8_st1) = u32x4{w[4], w[5], w[6], w[7]};
+  };
+  // Loads of the group's K(n+1) and V (tile indices within its half): bf16 V(n)
+  // by DMA; e4m3 V(n+1) (group 0, which stores it in M(n+1)) or V(n) (group 1,
+  // which stores it in M(n)) into registers.
   auto dma_phase = [&](int n, unsigned char* k_dst, unsigned char* v_dst) {
-    if (n + 1 < n_mine) dma_tile(kbase, k_tile, lo + n + 1, k_limit, kdma_off, k_dst + dma_dst);
-    if (n < n_mine) dma_tile(vbase, v_tile, lo + n, v_limit, vdma_off, v_dst + dma_dst);
+    if (n + 1 < n_mine) dma_tile<KDMA>(kbase, k_tile, lo + n + 1, k_limit, kdma_off, k_dst + kdma_dst);
+    if constexpr (FP8) {
+      load_v8(group == 0 ? n + 1 : n);
+    } else {
+      if (n < n_mine) dma_tile<DMA>(vbase, v_tile, lo + n, v_limit, vdma_off, v_dst + dma_dst);
+    }
+  };
+  // (bf16: nothing; the DMA writes the slot)
+  auto store_v = [&](int n, unsigned char* dst) {
+    if constexpr (FP8) store_v8(n, dst);
   };
 
   // ---- global phases --------------------------------------------------------
@@ -358,41 +445,50 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
   // last, which would follow M(2 n_trips), a phase past every wave's last tile).
   const int n_trips = (h + 2) / 2;  // covers M(0..h) and V(0..h-1) of the longer half
   if (group == 0) {
-    if (n_mine > 0) dma_tile(kbase, k_tile, lo, k_limit, kdma_off, k0_lds0 + dma_dst);
+    if (n_mine > 0) dma_tile<KDMA>(kbase, k_tile, lo, k_limit, kdma_off, k0_lds0 + kdma_dst);
+    if constexpr (FP8) load_v8(0);
     barrier_after<kWaitVm0Lgkm0>();
     m_first(k0_lds0);
+    store_v(0, v0_lds0);
     dma_phase(0, k0_lds1, v0_lds0);
     barrier_after<kWaitLgkm0>();
     for (int k = 0; k < n_trips; ++k) {
       v_phase(2 * k);
       barrier_after<kWaitVm0Lgkm0>();
       m_phase(2 * k + 1, k0_lds1, v0_lds0);
+      store_v(2 * k + 1, v0_lds1);
       dma_phase(2 * k + 1, k0_lds0, v0_lds1);
       barrier_after<kWaitLgkm0>();
       v_phase(2 * k + 1);
       barrier_after<kWaitVm0Lgkm0>();
       m_phase(2 * k + 2, k0_lds0, v0_lds1);
+      store_v(2 * k + 2, v0_lds0);
       dma_phase(2 * k + 2, k0_lds1, v0_lds0);
       barrier_after<kWaitLgkm0>();
     }
   } else {
-    if (n_mine > 0) dma_tile(kbase, k_tile, lo, k_limit, kdma_off, k1_lds0 + dma_dst);
+    if (n_mine > 0) dma_tile<KDMA>(kbase, k_tile, lo, k_limit, kdma_off, k1_lds0 + kdma_dst);
     barrier_after<kWaitVm0Lgkm0>();
     dma_phase(0, k1_lds1, v1_lds0);  // phase 0: no score tile yet
     barrier_after<kWaitLgkm0>();
     m_first(k1_lds0);
+    store_v(0, v1_lds0);
     barrier_after<kWaitVm0Lgkm0>();
     for (int k = 0; k < n_trips; ++k) {
       dma_phase(2 * k + 1, k1_lds0, v1_lds1);
       v_phase(2 * k);
       barrier_after<kWaitLgkm0>();
       m_phase(2 * k + 1, k1_lds1, v1_lds0);
+      store_v(2 * k + 1, v1_lds1);
       barrier_after<kWaitVm0Lgkm0>();
       dma_phase(2 * k + 2, k1_lds1, v1_lds0);
       v_phase(2 * k + 1);
       barrier_after<kWaitLgkm0>();
       m_phase(2 * k + 2, k1_lds0, v1_lds1);
-      if (k + 1 < n_trips) barrier_after<kWaitVm0Lgkm0>();  // M(2 n_trips) is past every T
+      if (k + 1 < n_trips) {  // M(2 n_trips) is past every T, and V(2 n_trips) past the half
+        store_v(2 * k + 2, v1_lds0);
+        barrier_after<kWaitVm0Lgkm0>();
+      }
     }
   }
   barrier_after<kWaitVm0Lgkm0>();  // every slot idle
@@ -403,7 +499,10 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
   // float when no key of the half was visible) and row sums in k1_lds0; the
   // group 0 wave of the same rows rescales both halves to the larger
   // reference and adds.
-  unsigned char* const acc_slot = si == 0 ? k0_lds0 : si == 1 ? k0_lds1 : si == 2 ? v0_lds0 : v0_lds1;
+  // (8 KB regions: group 0's K and V slots, or with e4m3 K, whose slots are
+  // 4 KB, the four V slots)
+  unsigned char* const acc_slot = FP8 ? (si == 0 ? v0_lds0 : si == 1 ? v0_lds1 : si == 2 ? v1_lds0 : v1_lds1)
+                                      : (si == 0 ? k0_lds0 : si == 1 ? k0_lds1 : si == 2 ? v0_lds0 : v0_lds1);
   float* const m_acc = (float*)acc_slot;
   float* const m_ml = (float*)k1_lds0 + si * 128;
   if (group == 1) {
@@ -427,11 +526,13 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
   const float l_tot = halfwave_sum(l_run * fa + l_b * fb);
 
   // ---- epilogue -------------------------------------------------------------
-  // O = acc / l rounded to bf16, staged through LDS (group 1's V slots, idle
-  // now; 4 KB per wave) and read back as whole rows for 1 KB row stores with
-  // the non-temporal hint. 16-byte chunks are XOR-swizzled by row.
-  const float inv = 1.0f / l_tot;
-  unsigned char* stage = (si < 2 ? v1_lds0 : v1_lds1) + (si & 1) * (32 * RB);
+  // O = acc / l rounded to bf16 (times the descale of e4m3 V, else 1), staged
+  // through LDS and read back as whole rows for 1 KB row stores with the
+  // non-temporal hint; 16-byte chunks are XOR-swizzled by row. The stage (4 KB)
+  // is the region this wave has just read its partner's state from: no other
+  // wave uses it after the barrier, and the wave's own reads return first.
+  const float inv = p.o_scale / l_tot;
+  unsigned char* stage = acc_slot;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -455,14 +556,23 @@ void attn_fwd_bf16_pp64_kernel(const AttnParams p) {
 
 }  // namespace pp64
 
-hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
-  // Same grid as the four-wave d = 64 kernel: ceil(Sq / 128) x B x Hq workgroups.
+template <bool FP8>
+static hipError_t launch_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
+  // Same grid as the four-wave d = 64 kernels: ceil(Sq / 128) x B x Hq workgroups.
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
   AttnParams arg = p;
   void* args[] = {&arg};
-  const void* fn = causal ? (const void*)&pp64::attn_fwd_bf16_pp64_kernel<true>
-                          : (const void*)&pp64::attn_fwd_bf16_pp64_kernel<false>;
+  const void* fn = causal ? (const void*)&pp64::attn_fwd_pp64_kernel<FP8, true>
+                          : (const void*)&pp64::attn_fwd_pp64_kernel<FP8, false>;
   return hipLaunchKernel(fn, dim3(grid), dim3(512), args, 0, stream);
+}
+
+hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
+  return launch_pp64<false>(p, causal, stream);
+}
+
+hipError_t launch_attn_fp8_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
+  return launch_pp64<true>(p, causal, stream);
 }
 
 }  // namespace sdpa18

@@ -98,6 +98,20 @@ def test_bf16_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
     log(f"  {stats}")
 
 
+# The same kernel on e4m3 inputs (scores on the fp8 matrix cores, V widened
+# exactly to bf16 on its way into LDS, P.V in bf16): the forms above that cover
+# odd tile counts, ragged tails, hidden second halves and GQA/MQA.
+FP8_PP64_FORMS = [(1, 4, 2, 1000, 1040, True), (2, 4, 2, 300, 1100, False), (1, 8, 2, 130, 1500, True),
+                  (1, 8, 1, 1024, 1024, True), (2, 3, 1, 2000, 2000, False)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", FP8_PP64_FORMS)
+def test_fp8_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
+    stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, 64, "fp8", causal, seed=33000 + Sq + Sk + Hq,
+                                         want_lse=True))
+    log(f"  {stats}")
+
+
 def test_bf16_d64_ping_pong_without_lse(gpu):
     """The same kernel with no lse output requested (the store is skipped)."""
     _run_full(sdpa_inputs.custom(2, 4, 2, 700, 1300, 64, "bf16", True, seed=32500), want_lse=False)
