@@ -60,11 +60,11 @@ def test_codelab_layout_key_split(gpu, d, causal):
     assert torch.equal(o_bhsd, o_ref) and torch.equal(lse, lse_ref)
 
 
-@pytest.mark.parametrize("causal", (False, True))
-def test_codelab_layout_ping_pong(gpu, causal):
-    """bf16 at d = 64 with 1100 keys on a small grid: the eight-wave ping-pong kernel reads and
-    writes (B, T, N, H) in place and equals its dense result bit for bit."""
-    w = sdpa_inputs.custom(2, 4, 2, 1100, 1100, 64, "bf16", causal, seed=15600, want_lse=True)
+@pytest.mark.parametrize("dtype,causal", list(itertools.product(("bf16", "fp8"), (False, True))))
+def test_codelab_layout_ping_pong(gpu, dtype, causal):
+    """bf16 and e4m3 at d = 64 with 1100 keys on a small grid: the eight-wave ping-pong kernel
+    reads and writes (B, T, N, H) in place and equals its dense result bit for bit."""
+    w = sdpa_inputs.custom(2, 4, 2, 1100, 1100, 64, dtype, causal, seed=15600, want_lse=True)
     log(f"[strided] {w.name} bshd ping-pong")
     inp = sdpa_inputs.make_inputs(w)
     dev = to_device(inp)
