@@ -98,8 +98,8 @@ def kernel_name(w) -> str:
         return "attn_bwd_dkdv_kernel"
     if w.dtype == "bf16" and w.d == 128:
         return "attn_fwd_bf16_pp_kernel"
-    if w.dtype in ("bf16", "fp8") and w.d == 64 and (w.Sq + 127) // 128 * w.B * w.Hq <= 768 and w.Sk >= 1024:
-        return "attn_fwd_pp64_kernel"  # d = 64 grids of up to 768 workgroups over 1024+ keys
+    if w.d == 64 and w.Sk >= 1024 and (w.dtype == "fp8" or (w.dtype == "bf16" and (w.Sq + 127) // 128 * w.B * w.Hq <= 768)):
+        return "attn_fwd_pp64_kernel"  # d = 64 over 1024+ keys (bf16: grids of up to 768 workgroups)
     if w.dtype == "fp8" and w.d == 128:
         return "attn_fwd_fp8_pp_kernel"
     if w.dtype == "f32" and (w.Sq + 127) // 128 * w.B * w.Hq <= 128 and w.Sk > 32:

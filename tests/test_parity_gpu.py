@@ -99,10 +99,11 @@ def test_bf16_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
 
 
 # The same kernel on e4m3 inputs (scores on the fp8 matrix cores, V widened
-# exactly to bf16 on its way into LDS, P.V in bf16): the forms above that cover
-# odd tile counts, ragged tails, hidden second halves and GQA/MQA.
+# exactly to bf16 on its way into LDS, P.V in bf16), which runs from 1024 keys
+# on any grid: the forms above that cover odd tile counts, ragged tails, hidden
+# second halves and GQA/MQA, and a grid of 1024 workgroups.
 FP8_PP64_FORMS = [(1, 4, 2, 1000, 1040, True), (2, 4, 2, 300, 1100, False), (1, 8, 2, 130, 1500, True),
-                  (1, 8, 1, 1024, 1024, True), (2, 3, 1, 2000, 2000, False)]
+                  (1, 8, 1, 1024, 1024, True), (2, 3, 1, 2000, 2000, False), (8, 16, 4, 1024, 1024, False)]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", FP8_PP64_FORMS)
