@@ -71,7 +71,7 @@ def log(msg: str) -> None:
 
 # Source file of each kernel family; its counter summaries are keyed on it.
 KERNEL_SOURCES = {"attn_fwd_bf16_pp_kernel": "attn_fwd_bf16_pp.hip", "attn_fwd_bf16_kernel": "attn_fwd_bf16.hip",
-                  "attn_fwd_pp64_kernel": "attn_fwd_pp64.hip",
+                  "attn_fwd_ppk_kernel": "attn_fwd_ppk.hip",
                   "attn_fwd_fp8_pp_kernel": "attn_fwd_fp8_pp.hip",
                   "attn_fwd_mfma_kernel": "attn_fwd_mfma.hip", "attn_fwd_f32_kernel": "attn_fwd_f32.hip",
                   "attn_fwd_f32_split_kernel": "attn_fwd_f32.hip",
@@ -97,9 +97,10 @@ def kernel_name(w) -> str:
     if w.path == "bwd":
         return "attn_bwd_dkdv_kernel"
     if w.dtype == "bf16" and w.d == 128:
-        return "attn_fwd_bf16_pp_kernel"
+        grid128 = (w.Sq + 127) // 128 * w.B * w.Hq
+        return "attn_fwd_bf16_pp_kernel" if grid128 > 256 else "attn_fwd_ppk_kernel"  # one pass over the CUs: key halves
     if w.d == 64 and w.Sk >= 1024 and (w.dtype == "fp8" or (w.dtype == "bf16" and (w.Sq + 127) // 128 * w.B * w.Hq <= 768)):
-        return "attn_fwd_pp64_kernel"  # d = 64 over 1024+ keys (bf16: grids of up to 768 workgroups)
+        return "attn_fwd_ppk_kernel"  # d = 64 over 1024+ keys (bf16: grids of up to 768 workgroups)
     if w.dtype == "fp8" and w.d == 128:
         return "attn_fwd_fp8_pp_kernel"
     if w.dtype == "f32" and (w.Sq + 127) // 128 * w.B * w.Hq <= 128 and w.Sk > 32:

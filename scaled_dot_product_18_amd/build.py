@@ -28,7 +28,7 @@ ARCH = "gfx950"
 
 PEAK_SOURCE = "mfma_peak.hip"
 PEAK_LIB_PATH = os.path.join(PKG_DIR, "libmfmapeak.so")
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_pp.hip", "attn_fwd_pp64.hip", "attn_fwd_fp8_pp.hip",
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_pp.hip", "attn_fwd_ppk.hip", "attn_fwd_fp8_pp.hip",
            "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_fwd_splitkv.hip", "attn_bwd.hip", "attn_bwd_f32.hip"]
 
 

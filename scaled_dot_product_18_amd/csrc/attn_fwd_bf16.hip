@@ -12,7 +12,7 @@
 // Layout of the work on CDNA4:
 //  * this kernel serves head dimensions 32 and 64 (the eight-wave ping-pong
 //    kernel in attn_fwd_bf16_pp.hip serves 128, and the one in
-//    attn_fwd_pp64.hip d = 64 grids of up to 768 workgroups over at
+//    attn_fwd_ppk.hip d = 64 grids of up to 768 workgroups over at
 //    least 1024 keys), in three forms picked by the grid: four waves with
 //    four resident per SIMD (large grids), four waves with the operand reads
 //    run ahead (up to 768 workgroups), and eight waves splitting the keys in
@@ -431,15 +431,15 @@ constexpr int kSplitMinKeys = 384;
 constexpr unsigned kPingPongMaxGrid = 768;
 constexpr int kPingPongMinKeys = 1024;
 
-// attn_fwd_pp64.hip: bf16, d = 64, eight waves in ping-pong over the two
-// halves of each workgroup's keys (n_qtiles counted in 128-row tiles, as here).
-hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream);
+// attn_fwd_ppk.hip: bf16, d = 64 or 128, eight waves in ping-pong over the
+// two halves of each workgroup's keys (n_qtiles counted in 128-row tiles).
+hipError_t launch_attn_bf16_ppk(const AttnParams& p, int d, bool causal, hipStream_t stream);
 
 template <int D, bool CAUSAL>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
   if (D == 64 && grid <= kPingPongMaxGrid && p.Sk >= kPingPongMinKeys)
-    return launch_attn_bf16_pp64(p, CAUSAL, stream);
+    return launch_attn_bf16_ppk(p, 64, CAUSAL, stream);
   AttnParams arg = p;
   void* args[] = {&arg};
   if (grid <= kSplitMaxGrid && p.Sk >= kSplitMinKeys)
@@ -452,9 +452,23 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 int bf16_block_m(int d) { return d == 128 ? bf16_pp_block_m() : Bf16Cfg<64>::BM; }
 
+// d = 128 shapes whose 128-row q-tiles fit in one pass over the 256 CUs
+// (ceil(Sq / 128) x B x Hq workgroups, one per CU) take the key-half ping-pong
+// kernel: twice the workgroups of the 256-row kernel, half the key tiles each
+// (A/B: B4 H8 T1024 29.0 -> 25.8 us unmasked, 27.7 -> 22.8 us causal; a grid of
+// 1024 loses, B16 H16 S512 47.5 -> 66.0 us). The rule does not depend on the
+// KV heads, so GQA and MHA on repeated K/V run the same kernel.
+constexpr unsigned kKeySplitMaxGrid128 = 256;
+
 hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream) {
-  // d = 128: the eight-wave ping-pong kernel (attn_fwd_bf16_pp.hip); d = 32 and 64 here.
-  if (d == 128) return launch_attn_bf16_pp(p, causal, stream);
+  // d = 128: the eight-wave ping-pong kernels (attn_fwd_bf16_pp.hip, attn_fwd_ppk.hip); d = 32 and 64 here.
+  if (d == 128) {
+    AttnParams q = p;
+    q.n_qtiles = (p.Sq + 127) / 128;
+    if ((unsigned)q.n_qtiles * (unsigned)p.B * (unsigned)p.Hq > kKeySplitMaxGrid128)
+      return launch_attn_bf16_pp(p, causal, stream);
+    return launch_attn_bf16_ppk(q, 128, causal, stream);
+  }
   if (d == 32) return causal ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
   return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }

@@ -2,7 +2,7 @@
 // at head dimensions 32 and 64 (fp8 MFMA for Q.K^T, bf16 MFMA for P.V with V
 // widened exactly); head dimension 128 runs the ping-pong kernel of
 // attn_fwd_fp8_pp.hip, and d = 64 over at least 1024 keys the one of
-// attn_fwd_pp64.hip. The fp8 MFMA has a K depth of 64: at d = 32 the upper
+// attn_fwd_ppk.hip. The fp8 MFMA has a K depth of 64: at d = 32 the upper
 // half-wave supplies zero operands, so each score is still one instruction.
 // The template also has a bf16-input form (FP8 = false), which nothing
 // launches.
@@ -343,15 +343,15 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 int fp8_block_m(int d) { return d == 128 ? fp8_pp_block_m() : 128; }
 
-// attn_fwd_pp64.hip: the d = 64 ping-pong kernel on e4m3 inputs, the grid of
+// attn_fwd_ppk.hip: the d = 64 ping-pong kernel on e4m3 inputs, the grid of
 // attn_fwd_mfma_kernel. Unlike bf16 it also wins on large grids (B8 H16 S2048:
 // 177 -> 156 us), where its scores run on the fp8 matrix cores.
-hipError_t launch_attn_fp8_pp64(const AttnParams& p, bool causal, hipStream_t stream);
+hipError_t launch_attn_fp8_ppk(const AttnParams& p, bool causal, hipStream_t stream);
 
 hipError_t launch_attn_fp8(const AttnParams& p, int d, bool causal, hipStream_t stream) {
   if (d == 128) return launch_attn_fp8_pp(p, causal, stream);
   if (d == 64 && p.Sk >= 1024)
-    return launch_attn_fp8_pp64(p, causal, stream);
+    return launch_attn_fp8_ppk(p, causal, stream);
   if (d == 32) return causal ? launch_one<32, true, true>(p, stream) : launch_one<32, false, true>(p, stream);
   return causal ? launch_one<64, true, true>(p, stream) : launch_one<64, false, true>(p, stream);
 }

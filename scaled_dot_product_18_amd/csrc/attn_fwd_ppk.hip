@@ -1,6 +1,7 @@
-// Fused scaled dot-product attention forward for gfx950 at head dim 64, on bf16
-// or fp8-e4m3fn inputs (bf16 output): eight waves in matrix-core / vector-unit
-// ping-pong over the two halves of a workgroup's keys.
+// Fused scaled dot-product attention forward for gfx950: eight waves in
+// matrix-core / vector-unit ping-pong over the two halves of a workgroup's
+// keys, at head dim 64 on bf16 or fp8-e4m3fn inputs and at head dim 128 on
+// bf16 (bf16 output).
 //
 // The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
 // and FlashAttention", section 3): K and V stream through on-chip tiles, the
@@ -13,8 +14,11 @@
 //
 // At d = 64 a tile's 16 MFMAs take half the time of its softmax on the vector
 // unit, and a wave that runs both in turn leaves each unit idle while it runs
-// the other. Here the two waves of a SIMD own the same 32 query rows and split
-// the workgroup's key tiles: group 0 (waves 0-3) takes the first half, group 1
+// the other. At d = 128 the 256-row ping-pong kernel of attn_fwd_bf16_pp.hip is
+// faster on large grids, but on grids that do not fill the CUs this kernel's
+// 128-row q-tiles double the workgroups and halve each one's chain of tiles.
+// Here the two waves of a SIMD own the same 32 query rows and split the
+// workgroup's key tiles: group 0 (waves 0-3) takes the first half, group 1
 // (waves 4-7) the second. Each wave's chain of phases
 //   M(m): O^T += V(m-1)^T . P(m-1)^T  and  S(m)^T = K(m) . Q^T - m_ref  (16 MFMAs; M0 only the scores)
 //   V(m): mask, P(m) = exp2(c S(m)), row sums, reference check
@@ -25,14 +29,16 @@
 // LDS and group 0 merges the two halves, as two blocks of the same softmax.
 //
 // K/V: each group streams its own tiles through its own two K and two V slots
-// (8 KB each, 64 KB for the workgroup with bf16 inputs). Both groups load their
-// K(n+1) and V(n) HBM -> LDS (buffer_load ... lds, 2 KB per wave) in global
-// phase 2n, group 0 after the MFMAs of its M(n), group 1 at the start of its
-// V(n-1), and wait for them at the barrier that ends phase 2n+1. Tile layouts
-// and swizzles are those of the four-wave d = 64 kernel: S^T and O^T are
-// computed transposed on v_mfma_f32_32x32x16_bf16 so that one lane owns one
-// query column, the bf16-rounded score accumulator is the P^T operand, and V^T
-// comes from the row-major V tile through ds_read_b64_tr_b16.
+// (8 KB each at d = 64, 64 KB for the workgroup with bf16 inputs; 16 KB and
+// 128 KB at d = 128). Both groups load their K(n+1) and V(n) HBM -> LDS
+// (buffer_load ... lds, 2 or 4 KB per wave and tensor) in global phase 2n,
+// group 0 after the MFMAs of its M(n), group 1 at the start of its V(n-1), and
+// wait for them at the barrier that ends phase 2n+1. Tile layouts and swizzles
+// are those of the four-wave d = 64 kernel and of the 256-row d = 128
+// ping-pong kernel: S^T and O^T are computed transposed on
+// v_mfma_f32_32x32x16_bf16 so that one lane owns one query column, the
+// bf16-rounded score accumulator is the P^T operand, and V^T comes from the
+// row-major V tile through ds_read_b64_tr_b16.
 //
 // e4m3 inputs: S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with unit
 // E8M0 scales, one MFMA per 32-key block (its K depth of 64 is the whole head
@@ -55,27 +61,17 @@
 #include "launch.h"
 
 namespace sdpa18 {
-namespace pp64 {
+namespace ppk {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int D = 64;
 constexpr int BM = 128;               // query rows per workgroup: four 32-row blocks, one per SIMD
 constexpr int BN = 64;                // keys per tile
-constexpr int RB = D * 2;             // bytes per bf16 K/V row in LDS
-constexpr int CH = RB / 16;           // 16-byte chunks per row
-constexpr int TILE = BN * RB;         // 8 KB
-constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide loads per tensor per wave (a group's 4 waves fill a tile)
-constexpr int RB8 = D;                // bytes per e4m3 K/V row
-constexpr int TILE8 = BN * RB8;       // 4 KB
 constexpr int kE8M0One = 127;         // E8M0 block scale 2^0 of the fp8 MFMA
 constexpr int KB = BN / 32;           // 32-key blocks of a score tile
 constexpr int KC = BN / 16;           // 16-key chunks (K depth of P.V)
-constexpr int DB = D / 32;            // 32-wide output blocks
-constexpr int QS = D / 16;            // MFMAs per 32x32 score block
-static_assert(DMA == 2, "4 waves x 2 loads cover an 8 KB tile");
 
 constexpr int LA = 4;  // MFMAs whose LDS operand reads are in flight ahead of the matrix core
 // A lane's partial row sum of one tile above this (or not finite) makes the
@@ -83,11 +79,16 @@ constexpr int LA = 4;  // MFMAs whose LDS operand reads are in flight ahead of t
 constexpr float kSumLimit = 4096.0f;
 constexpr int kBufferConfig = 0x00020000;  // word 3 of a raw buffer resource (gfx9 family)
 
-// XOR swizzles of the 16-byte chunks of a 128-byte K row (16 consecutive rows at
-// one logical chunk hit 8 distinct chunks on each bank half) and of a V row (the
-// 4 rows of a transposing read hit disjoint 32-byte pairs).
-__device__ __forceinline__ int k_swizzle(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int v_swizzle(int row) { return (0x6420 >> (4 * (row & 3))) & 15; }
+// XOR swizzles of the 16-byte chunks of a K row (16 consecutive rows at one
+// logical chunk hit 8 distinct chunks on each bank half of a 128-byte row, 16
+// distinct chunks of a 256-byte one) and of a V row (the 4 rows of a
+// transposing read hit disjoint 32-byte pairs).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) { return D == 128 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1)); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) {
+  return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
+}
 // e4m3 K rows (64 bytes, 4 chunks): 16 consecutive rows at one logical chunk hit
 // 4 rows per 256 bytes of banks, which the XOR with bits 2-3 of the row spreads.
 __device__ __forceinline__ int k8_swizzle(int row) { return (row >> 2) & 3; }
@@ -119,9 +120,18 @@ __device__ __forceinline__ void barrier_after() {
   asm volatile("" ::: "memory");
 }
 
-template <bool FP8, bool CAUSAL>
+template <int D, bool FP8, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_pp64_kernel(const AttnParams p) {
+void attn_fwd_ppk_kernel(const AttnParams p) {
+  static_assert(D == 64 || (D == 128 && !FP8), "head dims");
+  constexpr int RB = D * 2;             // bytes per bf16 K/V row in LDS
+  constexpr int CH = RB / 16;           // 16-byte chunks per row
+  constexpr int TILE = BN * RB;         // 8 or 16 KB
+  constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide loads per tensor per wave (a group's 4 waves fill a tile)
+  constexpr int RB8 = D;                // bytes per e4m3 K/V row
+  constexpr int TILE8 = BN * RB8;       // 4 KB
+  constexpr int DB = D / 32;            // 32-wide output blocks
+  constexpr int QS = D / 16;            // MFMAs per 32x32 score block
   constexpr int KTILE = FP8 ? TILE8 : TILE;     // K slot bytes
   constexpr int KDMA = KTILE / 1024 / 4;        // 1 KB K loads per wave
   constexpr int KCH = (FP8 ? RB8 : RB) / 16;    // 16-byte chunks per K row
@@ -197,12 +207,12 @@ void attn_fwd_pp64_kernel(const AttnParams p) {
 #pragma unroll
   for (int t = 0; t < KDMA; ++t) {
     const int row = (64 * (KDMA * si + t) + lane) / KCH;
-    kdma_off[t] = row * p.k_ss + 16 * ((lane % KCH) ^ (FP8 ? k8_swizzle(row) : k_swizzle(row)));
+    kdma_off[t] = row * p.k_ss + 16 * ((lane % KCH) ^ (FP8 ? k8_swizzle(row) : k_swizzle<D>(row)));
   }
 #pragma unroll
   for (int t = 0; t < DMA; ++t) {
     const int row = (64 * (DMA * si + t) + lane) / CH;
-    vdma_off[t] = row * p.v_ss + 16 * ((lane % CH) ^ v_swizzle(row));
+    vdma_off[t] = row * p.v_ss + 16 * ((lane % CH) ^ v_swizzle<D>(row));
   }
   const int kdma_dst = 1024 * KDMA * si, dma_dst = 1024 * DMA * si;
   // e4m3 V: lane l of wave si loads 16 codes, dims [16 (l%4), +16) of row
@@ -210,8 +220,8 @@ void attn_fwd_pp64_kernel(const AttnParams p) {
   // chunks of the row-major bf16 V tile.
   const int v8_row = 16 * si + (lane >> 2), v8_piece = lane & 3;
   const unsigned v8_ld = v8_row * p.v_ss + 16 * v8_piece;
-  const int v8_st0 = v8_row * RB + 16 * ((2 * v8_piece) ^ v_swizzle(v8_row));
-  const int v8_st1 = v8_row * RB + 16 * ((2 * v8_piece + 1) ^ v_swizzle(v8_row));
+  const int v8_st0 = v8_row * RB + 16 * ((2 * v8_piece) ^ v_swizzle<D>(v8_row));
+  const int v8_st1 = v8_row * RB + 16 * ((2 * v8_piece + 1) ^ v_swizzle<D>(v8_row));
   u32x4 v8reg = u32x4{0, 0, 0, 0};
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8) of row qi
@@ -236,14 +246,14 @@ void attn_fwd_pp64_kernel(const AttnParams p) {
   int k_rd[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s)
-    k_rd[s] = FP8 ? i32 * RB8 + 16 * ((2 * g + (s & 1)) ^ k8_swizzle(i32)) : i32 * RB + 16 * ((2 * s + g) ^ k_swizzle(i32));
+    k_rd[s] = FP8 ? i32 * RB8 + 16 * ((2 * g + (s & 1)) ^ k8_swizzle(i32)) : i32 * RB + 16 * ((2 * s + g) ^ k_swizzle<D>(i32));
   const int J = lane & 15;
   int v_rd[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int row = 4 * g + (J >> 2);
     const int d = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (J & 3);
-    v_rd[db] = row * RB + 16 * ((d >> 3) ^ v_swizzle(row)) + 2 * (d & 7);
+    v_rd[db] = row * RB + 16 * ((d >> 3) ^ v_swizzle<D>(row)) + 2 * (d & 7);
   }
 
   f32x16 acc[DB];
@@ -554,25 +564,26 @@ void attn_fwd_pp64_kernel(const AttnParams p) {
   if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_new + __log2f(l_tot)) * kLn2;
 }
 
-}  // namespace pp64
+}  // namespace ppk
 
-template <bool FP8>
-static hipError_t launch_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
+template <int D, bool FP8>
+static hipError_t launch_ppk(const AttnParams& p, bool causal, hipStream_t stream) {
   // Same grid as the four-wave d = 64 kernels: ceil(Sq / 128) x B x Hq workgroups.
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
   AttnParams arg = p;
   void* args[] = {&arg};
-  const void* fn = causal ? (const void*)&pp64::attn_fwd_pp64_kernel<FP8, true>
-                          : (const void*)&pp64::attn_fwd_pp64_kernel<FP8, false>;
+  const void* fn = causal ? (const void*)&ppk::attn_fwd_ppk_kernel<D, FP8, true>
+                          : (const void*)&ppk::attn_fwd_ppk_kernel<D, FP8, false>;
   return hipLaunchKernel(fn, dim3(grid), dim3(512), args, 0, stream);
 }
 
-hipError_t launch_attn_bf16_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
-  return launch_pp64<false>(p, causal, stream);
+hipError_t launch_attn_bf16_ppk(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+  return d == 128 ? launch_ppk<128, false>(p, causal, stream) : launch_ppk<64, false>(p, causal, stream);
 }
 
-hipError_t launch_attn_fp8_pp64(const AttnParams& p, bool causal, hipStream_t stream) {
-  return launch_pp64<true>(p, causal, stream);
+hipError_t launch_attn_fp8_ppk(const AttnParams& p, bool causal, hipStream_t stream) {
+  return launch_ppk<64, true>(p, causal, stream);
 }
 
 }  // namespace sdpa18
+

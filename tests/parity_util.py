@@ -74,11 +74,15 @@ def kernel_block_m(w) -> int:
     """Query rows per head of one workgroup of the kernel the launcher picks for
     ``w``: the d = 128 bf16 and fp8 kernels take 256-row tiles, the others 128;
     the causal d = 128 bf16 kernel packs 4 (2) query heads of one KV head into
-    a workgroup when the group size divides by 4 (2), 64 (128) rows each."""
-    if w.d == 128 and w.dtype == "bf16" and w.causal:
+    a workgroup when the group size divides by 4 (2), 64 (128) rows each. d = 128
+    bf16 shapes of at most 256 q-tiles of 128 rows (over all heads and batches)
+    run the key-half kernel on those tiles instead."""
+    if w.d == 128 and w.dtype == "bf16":
+        if (w.Sq + 127) // 128 * w.B * w.Hq <= 256:
+            return 128
         G = w.Hq // w.Hkv
-        return 64 if G % 4 == 0 else 128 if G % 2 == 0 else 256
-    return 256 if (w.d == 128 and w.dtype in ("bf16", "fp8")) else 128
+        return 256 // (1 if not w.causal else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1)
+    return 256 if (w.d == 128 and w.dtype == "fp8") else 128
 
 
 def log(msg: str) -> None:
