@@ -96,9 +96,10 @@ def kernel_name(w) -> str:
         return "attn_fwd_splitkv_kernel"
     if w.path == "bwd":
         return "attn_bwd_dkdv_kernel"
+    if w.dtype in ("bf16", "fp8") and w.d == 128 and (w.Sq + 127) // 128 * w.B * w.Hq <= (512 if w.causal else 256):
+        return "attn_fwd_ppk_kernel"  # small grids of 128-row tiles: key halves
     if w.dtype == "bf16" and w.d == 128:
-        grid128 = (w.Sq + 127) // 128 * w.B * w.Hq
-        return "attn_fwd_bf16_pp_kernel" if grid128 > 256 else "attn_fwd_ppk_kernel"  # one pass over the CUs: key halves
+        return "attn_fwd_bf16_pp_kernel"
     if w.d == 64 and w.Sk >= 1024 and (w.dtype == "fp8" or (w.dtype == "bf16" and (w.Sq + 127) // 128 * w.B * w.Hq <= 768)):
         return "attn_fwd_ppk_kernel"  # d = 64 over 1024+ keys (bf16: grids of up to 768 workgroups)
     if w.dtype == "fp8" and w.d == 128:

@@ -452,21 +452,16 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 int bf16_block_m(int d) { return d == 128 ? bf16_pp_block_m() : Bf16Cfg<64>::BM; }
 
-// d = 128 shapes whose 128-row q-tiles fit in one pass over the 256 CUs
-// (ceil(Sq / 128) x B x Hq workgroups, one per CU) take the key-half ping-pong
-// kernel: twice the workgroups of the 256-row kernel, half the key tiles each
-// (A/B: B4 H8 T1024 29.0 -> 25.8 us unmasked, 27.7 -> 22.8 us causal; a grid of
-// 1024 loses, B16 H16 S512 47.5 -> 66.0 us). The rule does not depend on the
-// KV heads, so GQA and MHA on repeated K/V run the same kernel.
-constexpr unsigned kKeySplitMaxGrid128 = 256;
+// attn_fwd_ppk.hip: whether a d = 128 shape is small enough for the key-half
+// kernel (twice the workgroups of the 256-row kernel, half the key tiles each).
+bool ppk_takes_d128(const AttnParams& p, bool causal);
 
 hipError_t launch_attn_bf16(const AttnParams& p, int d, bool causal, hipStream_t stream) {
   // d = 128: the eight-wave ping-pong kernels (attn_fwd_bf16_pp.hip, attn_fwd_ppk.hip); d = 32 and 64 here.
   if (d == 128) {
+    if (!ppk_takes_d128(p, causal)) return launch_attn_bf16_pp(p, causal, stream);
     AttnParams q = p;
     q.n_qtiles = (p.Sq + 127) / 128;
-    if ((unsigned)q.n_qtiles * (unsigned)p.B * (unsigned)p.Hq > kKeySplitMaxGrid128)
-      return launch_attn_bf16_pp(p, causal, stream);
     return launch_attn_bf16_ppk(q, 128, causal, stream);
   }
   if (d == 32) return causal ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);

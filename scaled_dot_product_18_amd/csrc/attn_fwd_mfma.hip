@@ -343,15 +343,23 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 int fp8_block_m(int d) { return d == 128 ? fp8_pp_block_m() : 128; }
 
-// attn_fwd_ppk.hip: the d = 64 ping-pong kernel on e4m3 inputs, the grid of
-// attn_fwd_mfma_kernel. Unlike bf16 it also wins on large grids (B8 H16 S2048:
-// 177 -> 156 us), where its scores run on the fp8 matrix cores.
-hipError_t launch_attn_fp8_ppk(const AttnParams& p, bool causal, hipStream_t stream);
+// attn_fwd_ppk.hip: the key-half ping-pong kernel on e4m3 inputs, 128-row
+// q-tiles (the grid of attn_fwd_mfma_kernel). At d = 64, unlike bf16, it also
+// wins on large grids (B8 H16 S2048: 177 -> 156 us), where its scores run on
+// the fp8 matrix cores.
+hipError_t launch_attn_fp8_ppk(const AttnParams& p, int d, bool causal, hipStream_t stream);
+// Whether a d = 128 shape is small enough for it (else the 256-row fp8 kernel).
+bool ppk_takes_d128(const AttnParams& p, bool causal);
 
 hipError_t launch_attn_fp8(const AttnParams& p, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return launch_attn_fp8_pp(p, causal, stream);
+  if (d == 128) {
+    if (!ppk_takes_d128(p, causal)) return launch_attn_fp8_pp(p, causal, stream);
+    AttnParams q = p;
+    q.n_qtiles = (p.Sq + 127) / 128;
+    return launch_attn_fp8_ppk(q, 128, causal, stream);
+  }
   if (d == 64 && p.Sk >= 1024)
-    return launch_attn_fp8_ppk(p, causal, stream);
+    return launch_attn_fp8_ppk(p, 64, causal, stream);
   if (d == 32) return causal ? launch_one<32, true, true>(p, stream) : launch_one<32, false, true>(p, stream);
   return causal ? launch_one<64, true, true>(p, stream) : launch_one<64, false, true>(p, stream);
 }

@@ -1,7 +1,6 @@
 // Fused scaled dot-product attention forward for gfx950: eight waves in
 // matrix-core / vector-unit ping-pong over the two halves of a workgroup's
-// keys, at head dim 64 on bf16 or fp8-e4m3fn inputs and at head dim 128 on
-// bf16 (bf16 output).
+// keys, at head dims 64 and 128 on bf16 or fp8-e4m3fn inputs (bf16 output).
 //
 // The method is the FlashAttention forward pass ("Self-attention, CUDA kernels
 // and FlashAttention", section 3): K and V stream through on-chip tiles, the
@@ -41,13 +40,13 @@
 // row-major V tile through ds_read_b64_tr_b16.
 //
 // e4m3 inputs: S^T = K . Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-// E8M0 scales, one MFMA per 32-key block (its K depth of 64 is the whole head
-// dim), into the same accumulator layout, so the softmax, P and the P.V MFMAs
-// are those of the bf16 form. K tiles (4 KB of e4m3) go HBM -> LDS by DMA. V
-// tiles go HBM -> registers (16 codes per lane) and are widened exactly to
-// bf16 into the bf16 V layout at the end of an M phase, the short one at
-// d = 64: group 0 loads V(n+1) after its M(n) and stores it after its M(n+1),
-// group 1 loads V(n) at the start of its V(n-1) and stores it after its M(n).
+// E8M0 scales, d / 64 MFMAs per 32-key block (K depth 64), into the same
+// accumulator layout, so the softmax, P and the P.V MFMAs are those of the
+// bf16 form. K tiles (4 or 8 KB of e4m3) go HBM -> LDS by DMA. V tiles go HBM
+// -> registers (16 or 32 codes per lane) and are widened exactly to bf16 into
+// the bf16 V layout at the end of an M phase, the short one at d = 64: group 0
+// loads V(n+1) after its M(n) and stores it after its M(n+1), group 1 loads
+// V(n) at the start of its V(n-1) and stores it after its M(n).
 // The descales of Q and K are folded into the exponent's multiplier and that
 // of V into the final 1/l.
 //
@@ -89,9 +88,11 @@ template <int D>
 __device__ __forceinline__ int v_swizzle(int row) {
   return D == 128 ? ((0xCA60 >> (4 * (row & 3))) & 15) : ((0x6420 >> (4 * (row & 3))) & 15);
 }
-// e4m3 K rows (64 bytes, 4 chunks): 16 consecutive rows at one logical chunk hit
-// 4 rows per 256 bytes of banks, which the XOR with bits 2-3 of the row spreads.
-__device__ __forceinline__ int k8_swizzle(int row) { return (row >> 2) & 3; }
+// e4m3 K rows: at d = 64 (64 bytes, 4 chunks) 16 consecutive rows at one logical
+// chunk hit 4 rows per 256 bytes of banks, which the XOR with bits 2-3 of the row
+// spreads; at d = 128 (128 bytes) the rows are laid out as bf16 rows at d = 64.
+template <int D>
+__device__ __forceinline__ int k8_swizzle(int row) { return D == 128 ? k_swizzle<64>(row) : ((row >> 2) & 3); }
 
 // This wave's share of one K or V tile, HBM -> LDS: lane l of load t fills the
 // 16 bytes at dst + 1024 t + 16 l. The buffer starts at the tile's first row
@@ -123,13 +124,16 @@ __device__ __forceinline__ void barrier_after() {
 template <int D, bool FP8, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_ppk_kernel(const AttnParams p) {
-  static_assert(D == 64 || (D == 128 && !FP8), "head dims");
+  static_assert(D == 64 || D == 128, "head dims");
   constexpr int RB = D * 2;             // bytes per bf16 K/V row in LDS
   constexpr int CH = RB / 16;           // 16-byte chunks per row
   constexpr int TILE = BN * RB;         // 8 or 16 KB
   constexpr int DMA = TILE / 1024 / 4;  // 1 KB wave-wide loads per tensor per wave (a group's 4 waves fill a tile)
   constexpr int RB8 = D;                // bytes per e4m3 K/V row
-  constexpr int TILE8 = BN * RB8;       // 4 KB
+  constexpr int TILE8 = BN * RB8;       // 4 or 8 KB
+  constexpr int QS8 = D / 64;           // e4m3 score MFMAs (K depth 64) per 32x32 score block
+  constexpr int PPR = RB8 / 16;         // 16-byte pieces of an e4m3 V row
+  constexpr int VL = PPR / 4;           // e4m3 V loads per lane and tile (a group's 256 lanes, 16 rows per wave)
   constexpr int DB = D / 32;            // 32-wide output blocks
   constexpr int QS = D / 16;            // MFMAs per 32x32 score block
   constexpr int KTILE = FP8 ? TILE8 : TILE;     // K slot bytes
@@ -207,7 +211,7 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
 #pragma unroll
   for (int t = 0; t < KDMA; ++t) {
     const int row = (64 * (KDMA * si + t) + lane) / KCH;
-    kdma_off[t] = row * p.k_ss + 16 * ((lane % KCH) ^ (FP8 ? k8_swizzle(row) : k_swizzle<D>(row)));
+    kdma_off[t] = row * p.k_ss + 16 * ((lane % KCH) ^ (FP8 ? k8_swizzle<D>(row) : k_swizzle<D>(row)));
   }
 #pragma unroll
   for (int t = 0; t < DMA; ++t) {
@@ -215,24 +219,34 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
     vdma_off[t] = row * p.v_ss + 16 * ((lane % CH) ^ v_swizzle<D>(row));
   }
   const int kdma_dst = 1024 * KDMA * si, dma_dst = 1024 * DMA * si;
-  // e4m3 V: lane l of wave si loads 16 codes, dims [16 (l%4), +16) of row
-  // 16 si + l/4, and stores them widened (exactly) to bf16 as two 16-byte
-  // chunks of the row-major bf16 V tile.
-  const int v8_row = 16 * si + (lane >> 2), v8_piece = lane & 3;
-  const unsigned v8_ld = v8_row * p.v_ss + 16 * v8_piece;
-  const int v8_st0 = v8_row * RB + 16 * ((2 * v8_piece) ^ v_swizzle<D>(v8_row));
-  const int v8_st1 = v8_row * RB + 16 * ((2 * v8_piece + 1) ^ v_swizzle<D>(v8_row));
-  u32x4 v8reg = u32x4{0, 0, 0, 0};
+  // e4m3 V: in load t lane l of wave si takes 16 codes, dims [16 (l % PPR), +16)
+  // of row 16 si + (64 / PPR) t + l / PPR, and stores them widened (exactly) to
+  // bf16 as two 16-byte chunks of the row-major bf16 V tile.
+  unsigned v8_ld[VL];
+  int v8_st0[VL], v8_st1[VL];
+  u32x4 v8reg[VL];
+#pragma unroll
+  for (int t = 0; t < VL; ++t) {
+    const int row = 16 * si + (64 / PPR) * t + lane / PPR, piece = lane % PPR;
+    v8_ld[t] = row * p.v_ss + 16 * piece;
+    v8_st0[t] = row * RB + 16 * ((2 * piece) ^ v_swizzle<D>(row));
+    v8_st1[t] = row * RB + 16 * ((2 * piece + 1) ^ v_swizzle<D>(row));
+    v8reg[t] = u32x4{0, 0, 0, 0};
+  }
 
   // ---- Q fragment (B operand of S^T): step s, half g holds dims [16s+8g, +8) of row qi
   const float c = p.qk_scale_log2;
   u32x4 qf[QS];
-  i32x8 qf8 = i32x8{};  // e4m3: dims [32g, +32) of row qi, the B operand of the fp8 score MFMA
+  i32x8 qf8[QS8];  // e4m3: step h holds dims [64h + 32g, +32) of row qi, the B operand of the fp8 score MFMA
   if constexpr (FP8) {
-    if (qi < p.Sq) {
-      const u32x4 a0 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * g);
-      const u32x4 a1 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * g + 16);
-      qf8 = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+#pragma unroll
+    for (int hs = 0; hs < QS8; ++hs) {
+      qf8[hs] = i32x8{};
+      if (qi < p.Sq) {
+        const u32x4 a0 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 64 * hs + 32 * g);
+        const u32x4 a1 = *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 64 * hs + 32 * g + 16);
+        qf8[hs] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      }
     }
   } else {
 #pragma unroll
@@ -240,13 +254,14 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
       qf[s] = (qi < p.Sq) ? *(const u32x4*)(qbase + (size_t)qi * p.q_ss + 32 * s + 16 * g) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- LDS operand offsets: K row 32kb + i32 at logical chunk 2s + g; V^T
-  // through the transposing read (lane J of a 16-lane group reads 4 dims of
-  // key row 4g + J/4).
+  // ---- LDS operand offsets: K row 32kb + i32 at logical chunk 2s + g (e4m3:
+  // chunk 4(s/2) + 2g + s%2); V^T through the transposing read (lane J of a
+  // 16-lane group reads 4 dims of key row 4g + J/4).
   int k_rd[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s)
-    k_rd[s] = FP8 ? i32 * RB8 + 16 * ((2 * g + (s & 1)) ^ k8_swizzle(i32)) : i32 * RB + 16 * ((2 * s + g) ^ k_swizzle<D>(i32));
+    k_rd[s] = FP8 ? i32 * RB8 + 16 * ((4 * (s >> 1) + 2 * g + (s & 1)) ^ k8_swizzle<D>(i32))
+                  : i32 * RB + 16 * ((2 * s + g) ^ k_swizzle<D>(i32));
   const int J = lane & 15;
   int v_rd[DB];
 #pragma unroll
@@ -288,15 +303,18 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
   };
   auto qk_part = [&](const unsigned char* kl) {
     if constexpr (FP8) {
-      // one fp8 MFMA (K depth 64 = d) per 32-key block; lane (i32, g) supplies
-      // key row i32's dims [32g, +32)
+      // d / 64 fp8 MFMAs (K depth 64) per 32-key block; in step h lane (i32, g)
+      // supplies key row i32's dims [64h + 32g, +32)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 a0 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[0]);
-        const u32x4 a1 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[1]);
-        const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8, negm, 0, 0, 0, kE8M0One, 0, kE8M0One);
-      }
+      for (int hs = 0; hs < QS8; ++hs)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 a0 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[2 * hs]);
+          const u32x4 a1 = *(const u32x4*)(kl + kb * 32 * RB8 + k_rd[2 * hs + 1]);
+          const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[hs], hs == 0 ? negm : s[kb], 0, 0, 0,
+                                                                  kE8M0One, 0, kE8M0One);
+        }
     } else {
 #pragma unroll
       for (int st = 0; st < QS; ++st)
@@ -316,7 +334,7 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
     if (m > T) return;
     pv_part(vl);
     qk_part(kl);
-    constexpr int NQK = FP8 ? KB : KB * QS, RQK = FP8 ? 2 : 1;  // score MFMAs, reads per score MFMA
+    constexpr int NQK = FP8 ? KB * QS8 : KB * QS, RQK = FP8 ? 2 : 1;  // score MFMAs, reads per score MFMA
     constexpr int NPV = KC * DB, NMF = KC * DB + NQK;
     static_assert(LA <= NPV, "the prologue reads belong to P.V MFMAs");
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
@@ -415,19 +433,24 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
     if (n >= n_mine) return;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + (lo + n) * v_tile), (short)0, v_limit - (lo + n) * v_tile, kBufferConfig);
-    v8reg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, v8_ld, 0, 0));
+#pragma unroll
+    for (int t = 0; t < VL; ++t)
+      v8reg[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, v8_ld[t], 0, 0));
   };
   auto store_v8 = [&](int n, unsigned char* dst) {
     __builtin_amdgcn_sched_barrier(0);
     if (n >= n_mine) return;
-    uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[j], 1.0f, false));
-      w[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[j], 1.0f, true));
+    for (int t = 0; t < VL; ++t) {
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[t][j], 1.0f, false));
+        w[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v8reg[t][j], 1.0f, true));
+      }
+      *(u32x4*)(dst + v8_st0[t]) = u32x4{w[0], w[1], w[2], w[3]};
+      *(u32x4*)(dst + v8_st1[t]) = u32x4{w[4], w[5], w[6], w[7]};
     }
-    *(u32x4*)(dst + v8_st0) = u32x4{w[0], w[1], w[2], w[3]};
-    *(u32x4*)(dst + v8_st1) = u32x4{w[4], w[5], w[6], w[7]};
   };
   // Loads of the group's K(n+1) and V (tile indices within its half): bf16 V(n)
   // by DMA; e4m3 V(n+1) (group 0, which stores it in M(n+1)) or V(n) (group 1,
@@ -509,8 +532,8 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
   // float when no key of the half was visible) and row sums in k1_lds0; the
   // group 0 wave of the same rows rescales both halves to the larger
   // reference and adds.
-  // (8 KB regions: group 0's K and V slots, or with e4m3 K, whose slots are
-  // 4 KB, the four V slots)
+  // (4 KB per 32-wide output block: group 0's K and V slots, or with e4m3 K,
+  // whose slots are half the size, the four V slots)
   unsigned char* const acc_slot = FP8 ? (si == 0 ? v0_lds0 : si == 1 ? v0_lds1 : si == 2 ? v1_lds0 : v1_lds1)
                                       : (si == 0 ? k0_lds0 : si == 1 ? k0_lds1 : si == 2 ? v0_lds0 : v0_lds1);
   float* const m_acc = (float*)acc_slot;
@@ -538,7 +561,7 @@ void attn_fwd_ppk_kernel(const AttnParams p) {
   // ---- epilogue -------------------------------------------------------------
   // O = acc / l rounded to bf16 (times the descale of e4m3 V, else 1), staged
   // through LDS and read back as whole rows for 1 KB row stores with the
-  // non-temporal hint; 16-byte chunks are XOR-swizzled by row. The stage (4 KB)
+  // non-temporal hint; 16-byte chunks are XOR-swizzled by row. The stage (32 rows)
   // is the region this wave has just read its partner's state from: no other
   // wave uses it after the barrier, and the wave's own reads return first.
   const float inv = p.o_scale / l_tot;
@@ -577,12 +600,25 @@ static hipError_t launch_ppk(const AttnParams& p, bool causal, hipStream_t strea
   return hipLaunchKernel(fn, dim3(grid), dim3(512), args, 0, stream);
 }
 
+// d = 128: the shapes this kernel takes over from the 256-row ping-pong kernels
+// (bf16 and e4m3), counted in q-tiles of 128 rows over all heads and batches.
+// Unmasked, at most one pass over the 256 CUs; causal, at most two, since the
+// heaviest tiles start first and the light ones fill the second pass. A/B per
+// 128-row tile count (bf16 / e4m3): unmasked 256 tiles 29.0 -> 25.8 / 22.4 ->
+// 18.6 us, 384 tiles 34.6 -> 44.2 / 24.7 -> 34.5 us; causal 512 tiles (B2 H8/2
+// T4096) 90.4 -> 76.6 / 70.4 -> 58.1 us, 768 tiles 84.0 -> 98.6 / 61.1 -> 75.2 us.
+// The count ignores the KV heads, so GQA and MHA on repeated K/V run the same kernel.
+bool ppk_takes_d128(const AttnParams& p, bool causal) {
+  const long long tiles = (long long)((p.Sq + 127) / 128) * p.B * p.Hq;
+  return tiles <= (causal ? 512 : 256);
+}
+
 hipError_t launch_attn_bf16_ppk(const AttnParams& p, int d, bool causal, hipStream_t stream) {
   return d == 128 ? launch_ppk<128, false>(p, causal, stream) : launch_ppk<64, false>(p, causal, stream);
 }
 
-hipError_t launch_attn_fp8_ppk(const AttnParams& p, bool causal, hipStream_t stream) {
-  return launch_ppk<64, true>(p, causal, stream);
+hipError_t launch_attn_fp8_ppk(const AttnParams& p, int d, bool causal, hipStream_t stream) {
+  return d == 128 ? launch_ppk<128, true>(p, causal, stream) : launch_ppk<64, true>(p, causal, stream);
 }
 
 }  // namespace sdpa18

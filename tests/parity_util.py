@@ -33,9 +33,17 @@ P8_TILE = 256
 LOG2E = 1.4426950408889634
 
 
+def key_half_d128(w) -> bool:
+    """d = 128 shapes the key-half kernel takes: at most 256 q-tiles of 128 rows
+    over all heads and batches, 512 under the causal mask."""
+    return w.d == 128 and (w.Sq + 127) // 128 * w.B * w.Hq <= (512 if w.causal else 256)
+
+
 def p8_first_row(w):
-    """First query row whose P.V runs with P in e4m3, or None if no row does."""
-    if w.dtype != "fp8" or w.d != 128:
+    """First query row whose P.V runs with P in e4m3, or None if no row does
+    (only the 256-row d = 128 fp8 kernel rounds P to e4m3; the key-half kernel,
+    whose P is bf16, takes the small shapes)."""
+    if w.dtype != "fp8" or w.d != 128 or key_half_d128(w):
         return None
     n_qt = (w.Sq + P8_TILE - 1) // P8_TILE
     if not w.causal:
@@ -74,12 +82,11 @@ def kernel_block_m(w) -> int:
     """Query rows per head of one workgroup of the kernel the launcher picks for
     ``w``: the d = 128 bf16 and fp8 kernels take 256-row tiles, the others 128;
     the causal d = 128 bf16 kernel packs 4 (2) query heads of one KV head into
-    a workgroup when the group size divides by 4 (2), 64 (128) rows each. d = 128
-    bf16 shapes of at most 256 q-tiles of 128 rows (over all heads and batches)
-    run the key-half kernel on those tiles instead."""
+    a workgroup when the group size divides by 4 (2), 64 (128) rows each. Small
+    d = 128 bf16 and fp8 shapes run the key-half kernel on 128-row tiles instead."""
+    if w.dtype in ("bf16", "fp8") and key_half_d128(w):
+        return 128
     if w.d == 128 and w.dtype == "bf16":
-        if (w.Sq + 127) // 128 * w.B * w.Hq <= 256:
-            return 128
         G = w.Hq // w.Hkv
         return 256 // (1 if not w.causal else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1)
     return 256 if (w.d == 128 and w.dtype == "fp8") else 128

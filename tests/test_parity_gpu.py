@@ -113,21 +113,31 @@ def test_fp8_d64_ping_pong(gpu, B, Hq, Hkv, Sq, Sk, causal):
     log(f"  {stats}")
 
 
-# bf16 at d = 128 on at most 256 q-tiles of 128 rows: the same kernel, there
-# chosen over the 256-row ping-pong kernel. One key (group 1 with no tile), a
-# single ragged tile, odd and even tile counts, Sq < Sk under the causal mask
-# with an offset that is not a multiple of 32, GQA, MQA and an odd group, and
-# both sides of the 256-workgroup boundary (256: this kernel; 288: the other).
+# bf16 at d = 128 on at most 256 q-tiles of 128 rows (512 causal): the same
+# kernel, there chosen over the 256-row ping-pong kernel. One key (group 1 with
+# no tile), a single ragged tile, odd and even tile counts, Sq < Sk under the
+# causal mask with an offset that is not a multiple of 32, GQA, MQA and an odd
+# group, and both sides of each boundary (unmasked 256: this kernel, 288: the
+# other; causal 512 and 544).
 PP128_FORMS = [
     (1, 4, 1, 1, 1, False), (1, 4, 4, 33, 33, True), (1, 4, 2, 200, 130, False), (1, 8, 2, 1000, 1000, True),
     (2, 8, 2, 700, 3000, True), (2, 3, 1, 130, 2000, False), (4, 8, 8, 1024, 1024, False),
-    (4, 8, 8, 1025, 1025, True),
+    (4, 8, 8, 1025, 1025, False), (4, 8, 8, 2048, 2048, True), (4, 8, 8, 2049, 2049, True),
 ]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", PP128_FORMS)
 def test_bf16_d128_key_halves(gpu, B, Hq, Hkv, Sq, Sk, causal):
     stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, 128, "bf16", causal, seed=34000 + Sq + Sk + Hq,
+                                         want_lse=True))
+    log(f"  {stats}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", PP128_FORMS)
+def test_fp8_d128_key_halves(gpu, B, Hq, Hkv, Sq, Sk, causal):
+    """The same forms on e4m3 inputs: two fp8 score MFMAs per 32-key block, V
+    widened to bf16 in 32 codes per lane (past each boundary the 256-row fp8 kernel)."""
+    stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, 128, "fp8", causal, seed=35000 + Sq + Sk + Hq,
                                          want_lse=True))
     log(f"  {stats}")
 
