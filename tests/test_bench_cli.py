@@ -26,8 +26,9 @@ def test_more_than_one_gpu_is_refused(argv, env):
 
 def test_kernel_names_follow_the_launch_dispatch():
     """The dominant kernel per workload, as the launchers pick it: the eight-wave
-    ping-pong kernels at d=128, the four-wave kernels at d=64, the fp32 key-split
-    kernel for grids up to 128 workgroups of 128 query rows."""
+    ping-pong kernels at d=128 (the key-half one on small grids), the four-wave
+    kernels at d=64, the fp32 key-split kernel for grids up to 128 workgroups of
+    128 query rows."""
     W = sdpa_inputs.WORKLOADS
     assert bench.kernel_name(W["single_head_f32_s128_d64"]) == "attn_fwd_f32_split_kernel"
     assert bench.kernel_name(W["vit_b16_bf16_b32_h12_s196_d64"]) == "attn_fwd_bf16_kernel"
@@ -40,6 +41,14 @@ def test_kernel_names_follow_the_launch_dispatch():
     assert bench.kernel_name(f32(1, 128, 128)) == "attn_fwd_f32_split_kernel"
     assert bench.kernel_name(f32(1, 129, 128)) == "attn_fwd_f32_kernel"
     assert bench.kernel_name(f32(1, 1, 32)) == "attn_fwd_f32_kernel"  # one key tile: nothing to split
+    # d = 128 key halves: at most 256 q-tiles of 128 rows unmasked, 512 causal, whatever the KV heads
+    w128 = lambda dt, Hkv, S, c: sdpa_inputs.custom(4, 8, Hkv, S, S, 128, dt, c, seed=0)  # noqa: E731
+    for dt, big in (("bf16", "attn_fwd_bf16_pp_kernel"), ("fp8", "attn_fwd_fp8_pp_kernel")):
+        for Hkv in (8, 2):
+            assert bench.kernel_name(w128(dt, Hkv, 1024, False)) == "attn_fwd_ppk_kernel"
+            assert bench.kernel_name(w128(dt, Hkv, 1025, False)) == big
+            assert bench.kernel_name(w128(dt, Hkv, 2048, True)) == "attn_fwd_ppk_kernel"
+            assert bench.kernel_name(w128(dt, Hkv, 2049, True)) == big
 
 
 def test_every_kernel_name_has_a_source():
