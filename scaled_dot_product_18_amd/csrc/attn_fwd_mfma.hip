@@ -31,6 +31,13 @@
 // double-buffered LDS ring (K row-major with an XOR swizzle, V transposed to
 // V^T with an XOR swizzle), one barrier per tile. Causal workgroups stop at the
 // diagonal and are launched heaviest first.
+//
+// SPLIT = 2: eight waves, the workgroup's key tiles in two halves. Waves 0-3
+// take the first half and waves 4-7 the second, each half with its own ring
+// and its own 256 threads staging it, so every SIMD runs two independent
+// chains of tiles; the two partial softmax states of a query row are merged
+// through LDS at the end. For grids of at most one workgroup per CU, where
+// one wave per SIMD would leave the chain of dependent steps exposed.
 #include "kernel_common.h"
 #include "launch.h"
 
@@ -63,14 +70,17 @@ struct MfmaCfg {
 // E8M0 scale byte 127 = 2^0: the scaled fp8 MFMA with unit scales.
 constexpr int kE8M0One = 127;
 
-template <int D, bool CAUSAL, bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+template <int D, bool CAUSAL, bool FP8, int SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256 * SPLIT, 256 * SPLIT), amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma_kernel(const AttnParams p) {
   using C = MfmaCfg<D, FP8>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SPLIT * 2 * C::STAGE];
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x & 255;  // thread within the key half: the staging assignment below
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave_id >> 2;      // key half (0 unless SPLIT = 2)
+  const int wave = wave_id & 3;       // 32-row block
   const int lane = tid & 63;
   const int i32 = lane & 31;  // MFMA row (A operand) / column (B operand, C)
   const int g = lane >> 5;    // half-wave
@@ -97,6 +107,11 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   const int n_tiles = (kv_end + C::BN - 1) / C::BN;
   const bool wave_active = qw < p.Sq;
   const int wave_tiles = !wave_active ? 0 : (CAUSAL ? min(n_tiles, (qw + 31 + p.causal_off) / C::BN + 1) : n_tiles);
+  // This half's key tiles [t_lo, t_hi), n_steps loop steps for both halves (the first takes the odd tile).
+  const int n_steps = SPLIT == 2 ? (n_tiles + 1) / 2 : n_tiles;
+  const int t_lo = half * n_steps;
+  const int t_hi = half == 0 ? n_steps : n_tiles;
+  unsigned char* const ring = smem + half * (2 * C::STAGE);
 
   // ---- Q fragment: B operand of S^T = K.Q^T, resident for the whole loop ---
   // bf16: step s, lane half g holds dims [16s + 8g, +8); fp8: dims [64s + 32g, +32).
@@ -191,22 +206,28 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-  float m_run = -INFINITY;  // running row max, in log2 units of the scaled score
+  // Running row max, in log2 units of the scaled score. It starts at the most
+  // negative float rather than -inf: a tile in which a row sees no key (the
+  // second key half under the causal mask) then rescales by exp2(0) and gives
+  // probabilities exp2(-inf) = 0, and the first tile with a visible key
+  // rescales the zero state by exp2(-FLT_MAX - m) = 0.
+  float m_run = -__FLT_MAX__;
   float l_run = 0.f;        // this lane's part of the running normaliser
   const float c = p.qk_scale_log2;
 
-  if (n_tiles > 0) {
-    stage_load(0);
-    stage_store(smem);
+  if (t_lo < t_hi) {
+    stage_load(t_lo * C::BN);
+    stage_store(ring);
   }
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  for (int i = 0; i < n_steps; ++i) {
+    const int kt = t_lo + i;
     const int kv0 = kt * C::BN;
-    if (kt + 1 < n_tiles) stage_load(kv0 + C::BN);
+    if (kt + 1 < t_hi) stage_load(kv0 + C::BN);
 
-    if (kt < wave_tiles) {
-      const unsigned char* kl = smem + (kt & 1) * C::STAGE;
+    if (kt < t_hi && kt < wave_tiles) {
+      const unsigned char* kl = ring + (i & 1) * C::STAGE;
       const unsigned char* vl = kl + C::KBYTES;
 
       // S^T = K . Q^T for BN keys x 32 queries.
@@ -296,21 +317,54 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
       }
     }
 
-    if (kt + 1 < n_tiles) stage_store(smem + ((kt + 1) & 1) * C::STAGE);
+    if (kt + 1 < t_hi) stage_store(ring + ((i + 1) & 1) * C::STAGE);
     __syncthreads();
+  }
+
+  // ---- merge of the two key halves (SPLIT = 2) -------------------------------
+  // The second half's waves leave acc, m_run and l_run in LDS (register-major,
+  // 64 lanes contiguous: acc from the start of the first ring, m and l at the
+  // end of the second); the first half's wave of the same rows rescales both
+  // to the larger reference and adds. A row always sees key 0, so the first
+  // half's reference is a real score maximum; a second half in which a row
+  // saw no key keeps -FLT_MAX and gets the factor 0.
+  if constexpr (SPLIT == 2) {
+    float* const m_acc = (float*)smem + wave * (C::DB * 16 * 64);
+    float* const m_ml = (float*)(smem + 4 * C::STAGE) - 8 * 64 + wave * (2 * 64);
+    static_assert(4 * C::DB * 16 * 64 * 4 + 8 * 64 * 4 <= 2 * C::STAGE, "merge state fits beside the stage");
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m_acc[(db * 16 + r) * 64 + lane] = acc[db][r];
+      m_ml[lane] = m_run;
+      m_ml[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (half == 1 || !wave_active) return;
+    const float m_b = m_ml[lane], l_b = m_ml[64 + lane];
+    const float m_new = fmaxf(m_run, m_b);
+    const float fa = exp2_fast(m_run - m_new), fb = exp2_fast(m_b - m_new);
+    m_run = m_new;
+    l_run = l_run * fa + l_b * fb;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * fa + m_acc[(db * 16 + r) * 64 + lane] * fb;
   }
 
   // ---- epilogue: normalise, round to bf16, store O (and lse) ---------------
   // A lane holds 4-dim pieces of one query row, so the wave writes its 32-row
-  // output tile to LDS (idle after the last barrier; wave w takes 32 * 2D
-  // bytes) and reads it back as whole rows: each global store then covers 1 KB
-  // of contiguous rows. 16-byte chunks are XOR-swizzled by row; the stores
+  // output tile to LDS (idle after the last barrier; with SPLIT = 2 the second
+  // ring, clear of the merge state; wave w takes 32 * 2D bytes) and reads it
+  // back as whole rows: each global store then covers 1 KB of contiguous rows. 16-byte chunks are XOR-swizzled by row; the stores
   // carry the non-temporal hint (nothing in the kernel reads O back).
   if (!wave_active) return;
   const float l_tot = halfwave_sum(l_run);
   const float inv = p.o_scale / l_tot;
   constexpr int ORB = 2 * D, OCH = ORB / 16;
-  unsigned char* stage = smem + wave * (32 * ORB);
+  static_assert(4 * 32 * ORB + 8 * 64 * 4 <= 2 * C::STAGE, "the output stage fits below the merge's m and l");
+  unsigned char* stage = smem + (SPLIT == 2 ? 2 * C::STAGE : 0) + wave * (32 * ORB);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -332,13 +386,22 @@ void attn_fwd_mfma_kernel(const AttnParams p) {
   if (g == 0 && qi < p.Sq && p.lse != nullptr) p.lse[qo_row0 + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
+// Grids of at most one workgroup per CU over at least 3 key tiles split the
+// keys over eight waves (the bf16 kernel's rule).
+constexpr unsigned kSplitMaxGrid = 256;
+constexpr int kSplitMinKeys = 384;
+
 template <int D, bool CAUSAL, bool FP8>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.n_qtiles * (unsigned)p.B * (unsigned)p.Hq;
   // hipLaunchKernel reports the status of this launch alone.
   AttnParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel((const void*)&attn_fwd_mfma_kernel<D, CAUSAL, FP8>, dim3(grid), dim3(256), args, 0, stream);
+  if (grid <= kSplitMaxGrid && p.Sk >= kSplitMinKeys)
+    return hipLaunchKernel((const void*)&attn_fwd_mfma_kernel<D, CAUSAL, FP8, 2>, dim3(grid), dim3(512), args, 0,
+                           stream);
+  return hipLaunchKernel((const void*)&attn_fwd_mfma_kernel<D, CAUSAL, FP8, 1>, dim3(grid), dim3(256), args, 0,
+                         stream);
 }
 
 int fp8_block_m(int d) { return d == 128 ? fp8_pp_block_m() : 128; }

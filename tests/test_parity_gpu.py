@@ -142,6 +142,24 @@ def test_fp8_d128_key_halves(gpu, B, Hq, Hkv, Sq, Sk, causal):
     log(f"  {stats}")
 
 
+# e4m3 at d = 32 and 64 below 1024 keys on grids of at most 256 workgroups of
+# 128 rows with at least 384 keys: the four-wave fp8 kernel's eight-wave key
+# split. Odd tile counts (3 tiles of 128: two in the first half), Sq < Sk with
+# the second half hidden from the first rows under the causal mask, GQA, MQA
+# and an odd group; the last form (288 workgroups) runs the four-wave form.
+FP8_SPLIT_FORMS = [(2, 4, 4, 384, 384, True), (1, 4, 2, 1000, 1000, True), (2, 4, 2, 300, 700, False),
+                   (1, 4, 2, 129, 900, True), (1, 8, 1, 500, 500, True), (2, 3, 1, 700, 700, False),
+                   (4, 8, 8, 1000, 1000, False), (9, 8, 8, 500, 500, True)]
+
+
+@pytest.mark.parametrize("d", (32, 64))
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,causal", FP8_SPLIT_FORMS)
+def test_fp8_key_split(gpu, d, B, Hq, Hkv, Sq, Sk, causal):
+    stats = _run_full(sdpa_inputs.custom(B, Hq, Hkv, Sq, Sk, d, "fp8", causal, seed=36000 + Sq + Sk + Hq + d,
+                                         want_lse=True))
+    log(f"  {stats}")
+
+
 def test_bf16_d128_key_halves_without_lse(gpu):
     """The d = 128 key-half kernel with no lse output requested."""
     _run_full(sdpa_inputs.custom(2, 4, 2, 700, 1300, 128, "bf16", True, seed=34500), want_lse=False)

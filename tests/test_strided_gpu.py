@@ -43,11 +43,11 @@ def test_codelab_layout_in_place(gpu, dtype, d, causal, S):
     assert torch.equal(o_bhsd, o_ref) and torch.equal(lse, lse_ref)
 
 
-@pytest.mark.parametrize("d,causal", list(itertools.product((32, 64), (False, True))))
-def test_codelab_layout_key_split(gpu, d, causal):
-    """bf16 at d = 32/64 with 700 keys on a small grid: the eight-wave key-split form reads and
-    writes (B, T, N, H) in place and equals its dense result bit for bit."""
-    w = sdpa_inputs.custom(2, 4, 2, 700, 700, d, "bf16", causal, seed=15500 + d, want_lse=True)
+@pytest.mark.parametrize("dtype,d,causal", list(itertools.product(("bf16", "fp8"), (32, 64), (False, True))))
+def test_codelab_layout_key_split(gpu, dtype, d, causal):
+    """bf16 and e4m3 at d = 32/64 with 700 keys on a small grid: the eight-wave key-split forms
+    read and write (B, T, N, H) in place and equal their dense results bit for bit."""
+    w = sdpa_inputs.custom(2, 4, 2, 700, 700, d, dtype, causal, seed=15500 + d, want_lse=True)
     log(f"[strided] {w.name} bshd split")
     inp = sdpa_inputs.make_inputs(w)
     dev = to_device(inp)
